@@ -1,0 +1,523 @@
+/*
+ * kvarn_oracle.c -- plain, slow CPU reference of the KVarN KV-cache quantizer
+ * hot path, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product (the HIP
+ * library under kv_cache_bit_token_amd/) never links, loads or calls it, and
+ * the two share no source, header, table or helper.
+ *
+ * Pages followed (cited by title and section):
+ *   [hotdry] "KVarN Hadamard 旋转与方差归一化：KV-cache 量化的校准算法实现"
+ *            (blog.hotdry.top)
+ *   [digest] "KVarN: 方差归一化的KV-Cache量化缓解推理任务中的误差累积"
+ *            (ai-feeds.com, paper digest of arXiv 2606.03458)
+ *   [deep]   "KV cache 為什麼能壓到 4-bit／2-bit 還不掉準確度——從 variance
+ *            normalization 講起" (vatt-ghern.pages.dev)
+ *
+ * Arithmetic is IEEE double throughout.  Values are rounded to binary16 only
+ * where the stored format holds binary16 (scales, zero points, row/column
+ * factors, and the dequantised output of the fp16 API).  Each quantisation
+ * code is decided in binary32, the precision of the GPU kernel that is
+ * compared against this file: the double value u is rounded to float and
+ * then to the nearest integer (ties to even).
+ *
+ * Readings of points the pages leave open (each one is listed in the design doc):
+ *   - A tile is 128 tokens x D channels; the rotation runs along channels
+ *     (head_dim) for K and for V ([hotdry] §Hadamard 旋转; [deep] stage card
+ *     "Hadamard rotation").
+ *   - The rotation is the Sylvester (natural order) Hadamard matrix scaled by
+ *     1/sqrt(D), i.e. orthonormal; no random sign flips.
+ *   - head_dim D0 that is not a power of two is zero-padded at the end to the
+ *     next power of two before rotation ([digest] §局限, first bullet).
+ *   - Normalisation: n_iters iterations of {column pass, row pass}; "std" is
+ *     the centred population standard deviation; log-factors accumulate as
+ *     l += ln(sigma), recomputed from the rotated tile each pass
+ *     ([hotdry] §迭代方差归一化 steps 1-3 and the log-space paragraph;
+ *     [deep] §四個步驟, Sinkhorn paragraph).
+ *   - A group whose values are all equal (exact comparison) has no spread to
+ *     normalise and keeps its factor.
+ *   - K is quantised per channel (over the 128 tokens), V per token (over the
+ *     D channels) ([hotdry] §非对称量化与尺度折叠; [deep] KEY/VALUE table).
+ *   - Asymmetric RTN: zero point = group min, scale = (max-min)/(2^b-1),
+ *     code = round((v-min)/scale), clamped ([deep] §為什麼樸素的 2-bit 量化,
+ *     worked 2-bit example).  A group with max == min gets scale 0, codes 0.
+ *   - Fold: the normalisation factor on the quantisation-group axis is
+ *     multiplied into that group's scale and zero point; the factor on the
+ *     other axis is stored on its own (RK per token for K, CV per channel for
+ *     V) ([hotdry] §非对称量化与尺度折叠: scales folded back on read).
+ *   - Packed layout (format v1): a b-bit code of element e sits at bit e*b of
+ *     the tile's byte stream, least significant bit first; K elements are
+ *     numbered e = t*D + j (token-major), V elements e = j*128 + t
+ *     (channel-major).  Meta per tile, binary16: K [SK(D) | ZK(D) | RK(128)],
+ *     V [SV(128) | ZV(128) | CV(D)].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define TILE 128
+
+/* ------------------------------------------------------------------------ */
+/* binary16 <-> double, written from the IEEE 754 binary16 layout:          */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.                  */
+/* ------------------------------------------------------------------------ */
+
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* 1.f * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round to nearest binary16, ties to even. */
+uint16_t oracle_double_to_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7e00;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: the quantum is 2^-24 */
+        double r = nearbyint(a * 16777216.0);
+        return sign | (uint16_t)r;   /* r == 1024 encodes the smallest normal */
+    }
+    int e;
+    frexp(a, &e);                    /* a = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                   /* a = 1.f * 2^E */
+    double r = nearbyint(ldexp(a, 10 - E));   /* in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard rotation ([hotdry] §Hadamard 旋转: H has entries +-1 and        */
+/* H H^T = n I; the product X H is computed by the fast Walsh-Hadamard       */
+/* transform in O(n log n)).                                                 */
+/* ------------------------------------------------------------------------ */
+
+int oracle_padded_dim(int d0)
+{
+    int d = 1;
+    while (d < d0)
+        d *= 2;
+    return d;
+}
+
+/* Sylvester construction: H[i][j] = (-1)^popcount(i & j). */
+int oracle_hadamard_entry(int i, int j)
+{
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+}
+
+/* In place x <- x H_n (unnormalised, natural order), n a power of two. */
+void oracle_fwht(double *x, int n)
+{
+    for (int h = 1; h < n; h *= 2)
+        for (int i = 0; i < n; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+}
+
+/* Pad each token row of a [128][d0] binary16 tile with zeros to D channels
+ * and rotate it: xt[t][:] = x_pad[t][:] H_D / sqrt(D). */
+void oracle_rotate_tile(const uint16_t *x, int d0, double *xt)
+{
+    int D = oracle_padded_dim(d0);
+    double inv = 1.0 / sqrt((double)D);
+    for (int t = 0; t < TILE; ++t) {
+        double *row = xt + (size_t)t * D;
+        for (int j = 0; j < D; ++j)
+            row[j] = (j < d0) ? oracle_half_to_double(x[(size_t)t * d0 + j]) : 0.0;
+        oracle_fwht(row, D);
+        for (int j = 0; j < D; ++j)
+            row[j] *= inv;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sinkhorn-style log-space normalisation ([hotdry] §迭代方差归一化: column  */
+/* pass, then row pass, repeated; scales kept as logs; [deep] §四個步驟).    */
+/* ------------------------------------------------------------------------ */
+
+static int all_equal(const double *v, int n)
+{
+    for (int i = 1; i < n; ++i)
+        if (v[i] != v[0])
+            return 0;
+    return 1;
+}
+
+/* Centred population standard deviation, two passes. */
+static double popstd(const double *v, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i)
+        s += v[i];
+    double m = s / n;
+    double q = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double d = v[i] - m;
+        q += d * d;
+    }
+    return sqrt(q / n);
+}
+
+/* xt: rotated tile [128][D].  Outputs the accumulated log-factors
+ * lr[128] (per token) and lc[D] (per channel); the normalised tile is
+ * Y[t][j] = xt[t][j] * exp(-lr[t] - lc[j]). */
+void oracle_normalise(const double *xt, int D, int n_iters, double *lr, double *lc)
+{
+    double grp[256];
+    for (int t = 0; t < TILE; ++t)
+        lr[t] = 0.0;
+    for (int j = 0; j < D; ++j)
+        lc[j] = 0.0;
+    for (int it = 0; it < n_iters; ++it) {
+        /* column pass: one std per channel, over the 128 tokens */
+        for (int j = 0; j < D; ++j) {
+            for (int t = 0; t < TILE; ++t)
+                grp[t] = xt[(size_t)t * D + j] * exp(-lr[t] - lc[j]);
+            if (all_equal(grp, TILE))
+                continue;
+            double sd = popstd(grp, TILE);
+            if (sd > 0.0)
+                lc[j] += log(sd);
+        }
+        /* row pass: one std per token, over the D channels */
+        for (int t = 0; t < TILE; ++t) {
+            for (int j = 0; j < D; ++j)
+                grp[j] = xt[(size_t)t * D + j] * exp(-lr[t] - lc[j]);
+            if (all_equal(grp, D))
+                continue;
+            double sd = popstd(grp, D);
+            if (sd > 0.0)
+                lr[t] += log(sd);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric round-to-nearest of one group ([deep] worked 2-bit example:   */
+/* range [min, max], 2^b levels, scale = (max - min)/(2^b - 1), code =       */
+/* round((v - min)/scale)).                                                  */
+/* v[i * stride], i < n.  Writes the zero point (min), the scale, the codes  */
+/* (codes[i * cstride]) and, if u != NULL, u[i * cstride] = (v - min)/scale. */
+/* ------------------------------------------------------------------------ */
+void oracle_rtn_group(const double *v, int n, int stride, int bits,
+                      double *z, double *s, uint8_t *codes, int cstride, double *u)
+{
+    double mn = v[0], mx = v[0];
+    for (int i = 1; i < n; ++i) {
+        double a = v[(size_t)i * stride];
+        if (a < mn) mn = a;
+        if (a > mx) mx = a;
+    }
+    int levels = (1 << bits) - 1;
+    double scale = (mx - mn) / levels;
+    *z = mn;
+    *s = scale;
+    for (int i = 0; i < n; ++i) {
+        double ui = (scale > 0.0) ? (v[(size_t)i * stride] - mn) / scale : 0.0;
+        float r = rintf((float)ui);               /* decided in binary32 */
+        if (r < 0.0f) r = 0.0f;
+        if (r > (float)levels) r = (float)levels;
+        codes[(size_t)i * cstride] = (uint8_t)r;
+        if (u)
+            u[(size_t)i * cstride] = ui;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bit packing, format v1 (see the header comment).                          */
+/* ------------------------------------------------------------------------ */
+
+int64_t oracle_code_bytes(int D, int bits) { return (int64_t)TILE * D * bits / 8; }
+
+int64_t oracle_meta_halves(int D, int is_key) { return is_key ? 2 * D + TILE : 2 * TILE + D; }
+
+void oracle_pack(const uint8_t *codes, int D, int bits, int is_key, uint8_t *out)
+{
+    memset(out, 0, (size_t)oracle_code_bytes(D, bits));
+    for (int t = 0; t < TILE; ++t)
+        for (int j = 0; j < D; ++j) {
+            int64_t e = is_key ? (int64_t)t * D + j : (int64_t)j * TILE + t;
+            int64_t bit = e * bits;
+            out[bit / 8] |= (uint8_t)(codes[(size_t)t * D + j] << (bit % 8));
+        }
+}
+
+void oracle_unpack(const uint8_t *packed, int D, int bits, int is_key, uint8_t *codes)
+{
+    int mask = (1 << bits) - 1;
+    for (int t = 0; t < TILE; ++t)
+        for (int j = 0; j < D; ++j) {
+            int64_t e = is_key ? (int64_t)t * D + j : (int64_t)j * TILE + t;
+            int64_t bit = e * bits;
+            codes[(size_t)t * D + j] = (uint8_t)((packed[bit / 8] >> (bit % 8)) & mask);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* One tile, end to end.                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Optional diagnostics, each NULL or sized as noted (D = padded dim). */
+typedef struct {
+    double *y;   /* [128][D] normalised values Y                       */
+    double *u;   /* [128][D] (Y - z)/s of each element                 */
+    double *z;   /* [G]  group zero points (G = D for K, 128 for V)    */
+    double *s;   /* [G]  group scales                                  */
+    double *lr;  /* [128] row log-factors                              */
+    double *lc;  /* [D]   column log-factors                           */
+} oracle_diag;
+
+/* Quantise one [128][d0] binary16 tile.  codes_packed: oracle_code_bytes;
+ * meta: oracle_meta_halves binary16 values. */
+void oracle_quantize_tile(const uint16_t *x, int d0, int bits, int n_iters, int is_key,
+                          uint8_t *codes_packed, uint16_t *meta, const oracle_diag *dg)
+{
+    int D = oracle_padded_dim(d0);
+    size_t n = (size_t)TILE * D;
+    double *xt = malloc(n * sizeof(double));
+    double *y = malloc(n * sizeof(double));
+    double *u = malloc(n * sizeof(double));
+    uint8_t *codes = malloc(n);
+    double lr[TILE], lc[256], z[256], s[256];
+
+    oracle_rotate_tile(x, d0, xt);
+    oracle_normalise(xt, D, n_iters, lr, lc);
+    for (int t = 0; t < TILE; ++t)
+        for (int j = 0; j < D; ++j)
+            y[(size_t)t * D + j] = xt[(size_t)t * D + j] * exp(-lr[t] - lc[j]);
+
+    if (is_key) {
+        /* K: one group per channel j, over the 128 tokens */
+        for (int j = 0; j < D; ++j)
+            oracle_rtn_group(y + j, TILE, D, bits, &z[j], &s[j], codes + j, D, u + j);
+        for (int j = 0; j < D; ++j) {
+            meta[j] = oracle_double_to_half(exp(lc[j]) * s[j]);           /* SK */
+            meta[D + j] = oracle_double_to_half(exp(lc[j]) * z[j]);       /* ZK */
+        }
+        for (int t = 0; t < TILE; ++t)
+            meta[2 * D + t] = oracle_double_to_half(exp(lr[t]));          /* RK */
+    } else {
+        /* V: one group per token t, over the D channels */
+        for (int t = 0; t < TILE; ++t)
+            oracle_rtn_group(y + (size_t)t * D, D, 1, bits, &z[t], &s[t],
+                             codes + (size_t)t * D, 1, u + (size_t)t * D);
+        for (int t = 0; t < TILE; ++t) {
+            meta[t] = oracle_double_to_half(exp(lr[t]) * s[t]);           /* SV */
+            meta[TILE + t] = oracle_double_to_half(exp(lr[t]) * z[t]);    /* ZV */
+        }
+        for (int j = 0; j < D; ++j)
+            meta[2 * TILE + j] = oracle_double_to_half(exp(lc[j]));       /* CV */
+    }
+    oracle_pack(codes, D, bits, is_key, codes_packed);
+
+    if (dg) {
+        int G = is_key ? D : TILE;
+        if (dg->y) memcpy(dg->y, y, n * sizeof(double));
+        if (dg->u) memcpy(dg->u, u, n * sizeof(double));
+        if (dg->z) memcpy(dg->z, z, G * sizeof(double));
+        if (dg->s) memcpy(dg->s, s, G * sizeof(double));
+        if (dg->lr) memcpy(dg->lr, lr, TILE * sizeof(double));
+        if (dg->lc) memcpy(dg->lc, lc, D * sizeof(double));
+    }
+    free(xt);
+    free(y);
+    free(u);
+    free(codes);
+}
+
+/* Dequantise one tile to double [128][d0]: rebuild the rotated-domain value
+ * from the stored binary16 fields (K: RK_t (code SK_j + ZK_j); V:
+ * CV_j (code SV_t + ZV_t)), then undo the rotation (the scaled Hadamard is
+ * symmetric and its own inverse) and keep the first d0 channels. */
+void oracle_dequantize_tile(const uint8_t *codes_packed, const uint16_t *meta, int d0,
+                            int bits, int is_key, double *out)
+{
+    int D = oracle_padded_dim(d0);
+    size_t n = (size_t)TILE * D;
+    uint8_t *codes = malloc(n);
+    double row[256];
+    double inv = 1.0 / sqrt((double)D);
+    oracle_unpack(codes_packed, D, bits, is_key, codes);
+    for (int t = 0; t < TILE; ++t) {
+        for (int j = 0; j < D; ++j) {
+            double c = codes[(size_t)t * D + j];
+            if (is_key) {
+                double sk = oracle_half_to_double(meta[j]);
+                double zk = oracle_half_to_double(meta[D + j]);
+                double rk = oracle_half_to_double(meta[2 * D + t]);
+                row[j] = rk * (c * sk + zk);
+            } else {
+                double sv = oracle_half_to_double(meta[t]);
+                double zv = oracle_half_to_double(meta[TILE + t]);
+                double cv = oracle_half_to_double(meta[2 * TILE + j]);
+                row[j] = cv * (c * sv + zv);
+            }
+        }
+        oracle_fwht(row, D);
+        for (int j = 0; j < d0; ++j)
+            out[(size_t)t * d0 + j] = row[j] * inv;
+    }
+    free(codes);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batched entry points (OpenMP over tiles; each tile is independent).       */
+/* ------------------------------------------------------------------------ */
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Quantise n_tiles tiles of one tensor ([n_tiles][128][d0] binary16).
+ * Diagnostics are optional (NULL) and, when given, sized per tile as in
+ * oracle_diag, concatenated over tiles. */
+void oracle_quantize_tiles(int64_t n_tiles, int d0, int bits, int n_iters, int is_key,
+                           const uint16_t *x, uint8_t *codes, uint16_t *meta,
+                           double *y, double *u, double *z, double *s,
+                           double *lr, double *lc)
+{
+    int D = oracle_padded_dim(d0);
+    int G = is_key ? D : TILE;
+    int64_t cb = oracle_code_bytes(D, bits);
+    int64_t mh = oracle_meta_halves(D, is_key);
+    size_t n = (size_t)TILE * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_tiles; ++i) {
+        oracle_diag dg = {
+            y ? y + i * n : NULL, u ? u + i * n : NULL,
+            z ? z + i * G : NULL, s ? s + i * G : NULL,
+            lr ? lr + i * TILE : NULL, lc ? lc + i * D : NULL,
+        };
+        oracle_quantize_tile(x + (size_t)i * TILE * d0, d0, bits, n_iters, is_key,
+                             codes + i * cb, meta + i * mh, &dg);
+    }
+}
+
+/* Dequantise n_tiles tiles; out_f64 and/or out_f16 ([n_tiles][128][d0]) may
+ * be NULL.  The binary16 output is the double result rounded to nearest. */
+void oracle_dequantize_tiles(int64_t n_tiles, int d0, int bits, int is_key,
+                             const uint8_t *codes, const uint16_t *meta,
+                             double *out_f64, uint16_t *out_f16)
+{
+    int D = oracle_padded_dim(d0);
+    int64_t cb = oracle_code_bytes(D, bits);
+    int64_t mh = oracle_meta_halves(D, is_key);
+    size_t n0 = (size_t)TILE * d0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_tiles; ++i) {
+        double *o = malloc(n0 * sizeof(double));
+        oracle_dequantize_tile(codes + i * cb, meta + i * mh, d0, bits, is_key, o);
+        if (out_f64)
+            memcpy(out_f64 + i * n0, o, n0 * sizeof(double));
+        if (out_f16)
+            for (size_t k = 0; k < n0; ++k)
+                out_f16[i * n0 + k] = oracle_double_to_half(o[k]);
+        free(o);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the quantised cache: the textbook formula applied   */
+/* to the dequantised (double, not rounded) K and V.  Query head h reads KV  */
+/* head h / (n_q_heads / n_kv_heads).  s_t = sm_scale * q . k_t;             */
+/* p = softmax(s) (max subtracted); o = sum_t p_t v_t.                       */
+/* Cache tile i of (b, g) is at index (b * n_kv_heads + g) * tiles_per_seq + i.
+ * q: [batch][n_q_heads][d0] binary16; out: [batch][n_q_heads][d0] double.   */
+/* ------------------------------------------------------------------------ */
+void oracle_decode_attention(int batch, int n_q_heads, int n_kv_heads, int tiles_per_seq,
+                             int d0, int k_bits, int v_bits, const uint16_t *q,
+                             const uint8_t *k_codes, const uint8_t *v_codes,
+                             const uint16_t *k_meta, const uint16_t *v_meta,
+                             double sm_scale, double *out)
+{
+    int D = oracle_padded_dim(d0);
+    int group = n_q_heads / n_kv_heads;
+    int64_t kcb = oracle_code_bytes(D, k_bits), vcb = oracle_code_bytes(D, v_bits);
+    int64_t kmh = oracle_meta_halves(D, 1), vmh = oracle_meta_halves(D, 0);
+    int64_t T = (int64_t)tiles_per_seq * TILE;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)batch * n_kv_heads; ++bg) {
+        int b = (int)(bg / n_kv_heads), g = (int)(bg % n_kv_heads);
+        double *K = malloc((size_t)T * d0 * sizeof(double));
+        double *V = malloc((size_t)T * d0 * sizeof(double));
+        double *sc = malloc((size_t)T * sizeof(double));
+        for (int i = 0; i < tiles_per_seq; ++i) {
+            int64_t tile = bg * tiles_per_seq + i;
+            oracle_dequantize_tile(k_codes + tile * kcb, k_meta + tile * kmh, d0, k_bits, 1,
+                                   K + (size_t)i * TILE * d0);
+            oracle_dequantize_tile(v_codes + tile * vcb, v_meta + tile * vmh, d0, v_bits, 0,
+                                   V + (size_t)i * TILE * d0);
+        }
+        for (int hh = 0; hh < group; ++hh) {
+            int h = g * group + hh;
+            const uint16_t *qh = q + ((size_t)b * n_q_heads + h) * d0;
+            double qd[256];
+            for (int j = 0; j < d0; ++j)
+                qd[j] = oracle_half_to_double(qh[j]);
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < T; ++t) {
+                double acc = 0.0;
+                for (int j = 0; j < d0; ++j)
+                    acc += qd[j] * K[(size_t)t * d0 + j];
+                sc[t] = sm_scale * acc;
+                if (sc[t] > mx) mx = sc[t];
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                sc[t] = exp(sc[t] - mx);
+                l += sc[t];
+            }
+            double *o = out + ((size_t)b * n_q_heads + h) * d0;
+            for (int j = 0; j < d0; ++j)
+                o[j] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                double p = sc[t] / l;
+                for (int j = 0; j < d0; ++j)
+                    o[j] += p * V[(size_t)t * d0 + j];
+            }
+        }
+        free(K);
+        free(V);
+        free(sc);
+    }
+}

@@ -1,0 +1,133 @@
+"""Pins of the oracle's dequantisation and decode attention.
+
+Pages: hotdry page (blog.hotdry.top) "非对称量化与尺度折叠" (scales multiplied
+back on read); digest page (ai-feeds.com) "方法", module 3 (dequantisation
+restores the scale; quantised-cache attention output close to full
+precision, the attention-output reconstruction proxy); deep-dive page
+(vatt-ghern.pages.dev) stage card "Hadamard rotation" (orthonormal, so
+attention inner products are unchanged) and the naive-RTN tab of the
+comparison widget (per-token RTN without outlier treatment).
+
+Attention is compared with torch's scaled_dot_product_attention in float64
+on the CPU (an independent library routine) applied to the oracle's own
+dequantised cache; the rotation identity q.k = (qH)(kH) is checked on the
+rotated-domain fields directly.
+"""
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from kv_cache_bit_token_amd import synthetic
+
+
+def _quantize_pair(k16, v16, n_iters=5, kb=4, vb=2):
+    kq = oracle.quantize_tiles(k16, kb, n_iters, True)
+    vq = oracle.quantize_tiles(v16, vb, n_iters, False)
+    return kq, vq
+
+
+@pytest.mark.parametrize("d0", [128, 96, 64])
+def test_reconstruction_within_rotated_bound(d0):
+    k, v = synthetic.outlier_kv_host(5, 1, 256, d0)
+    for x16, bits, is_key in ((k, 4, True), (v, 2, False)):
+        tiles = synthetic.as_tiles(x16)
+        q = oracle.quantize_tiles(tiles, bits, 5, is_key, diag=True)
+        o64, o16 = oracle.dequantize_tiles(q["codes"], q["meta"], d0, bits, is_key)
+        D = oracle.padded_dim(d0)
+        for i in range(tiles.shape[0]):
+            xt = oracle.rotate_tile(tiles[i])
+            c = oracle.unpack(q["codes"][i], D, bits, is_key).astype(np.float64)
+            m = q["meta"][i].astype(np.float64)
+            if is_key:
+                rot = m[2 * D:][:, None] * (c * m[:D][None, :] + m[D:2 * D][None, :])
+            else:
+                rot = m[256:][None, :] * (c * m[:128][:, None] + m[128:256][:, None])
+            # per-token L2 error is preserved by the orthonormal rotation; the
+            # first d0 channels can only carry less of it
+            err_rot = np.sqrt(((xt - rot) ** 2).sum(1))
+            err = np.sqrt(((tiles[i].astype(np.float64) - o64[i]) ** 2).sum(1))
+            assert np.all(err <= err_rot * (1 + 1e-9) + 1e-9)
+            # the binary16 output is the double output rounded to nearest
+            assert np.array_equal(o16[i], o64[i].astype(np.float16))
+
+
+def test_dequant_exact_grid_case():
+    # codes with unit scale, zero offset, unit factors: dequant = codes H / sqrt(D)
+    D = 128
+    rng = np.random.default_rng(0)
+    c = rng.integers(0, 16, size=(128, D)).astype(np.uint8)
+    meta = np.concatenate([np.ones(D), np.zeros(D), np.ones(128)]).astype(np.float16)
+    o64, _ = oracle.dequantize_tiles(oracle.pack(c, 4, True)[None], meta[None], D, 4, True)
+    ref = c.astype(np.float64) @ scipy.linalg.hadamard(D) / np.sqrt(D)
+    assert np.allclose(o64[0], ref, rtol=0, atol=1e-12)
+
+
+def _sdpa_ref(q16, Kd, Vd, n_kv):
+    # q [B][Hq][d0]; Kd, Vd [B*n_kv][T][d0]
+    B, Hq, d0 = q16.shape
+    T = Kd.shape[1]
+    q = torch.from_numpy(q16.astype(np.float64)).reshape(B, Hq, 1, d0)
+    K = torch.from_numpy(Kd).reshape(B, n_kv, T, d0).repeat_interleave(Hq // n_kv, dim=1)
+    V = torch.from_numpy(Vd).reshape(B, n_kv, T, d0).repeat_interleave(Hq // n_kv, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=1.0 / np.sqrt(d0))
+    return o.reshape(B, Hq, d0).numpy()
+
+
+@pytest.mark.parametrize("d0", [128, 96])
+def test_attention_is_textbook_softmax_attention(d0):
+    B, n_kv, Hq, T = 2, 2, 8, 512
+    k, v = synthetic.outlier_kv_host(9, B * n_kv, T, d0)
+    kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)
+    kq, vq = _quantize_pair(kt, vt)
+    q = synthetic.query_host(9, B, Hq, d0)
+    o = oracle.decode_attention(q, kq["codes"], vq["codes"], kq["meta"], vq["meta"],
+                                n_kv_heads=n_kv, tiles_per_seq=T // 128)
+    Kd, _ = oracle.dequantize_tiles(kq["codes"], kq["meta"], d0, 4, True)
+    Vd, _ = oracle.dequantize_tiles(vq["codes"], vq["meta"], d0, 2, False)
+    ref = _sdpa_ref(q, Kd.reshape(B * n_kv, T, d0), Vd.reshape(B * n_kv, T, d0), n_kv)
+    assert np.allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_rotation_preserves_scores():
+    d0 = 128
+    k, _ = synthetic.outlier_kv_host(2, 1, 128, d0)
+    kq = oracle.quantize_tiles(synthetic.as_tiles(k), 4, 5, True)
+    c = oracle.unpack(kq["codes"][0], d0, 4, True).astype(np.float64)
+    m = kq["meta"][0].astype(np.float64)
+    krot = m[2 * d0:][:, None] * (c * m[:d0][None, :] + m[d0:2 * d0][None, :])
+    kd, _ = oracle.dequantize_tiles(kq["codes"], kq["meta"], d0, 4, True)
+    q = np.random.default_rng(1).standard_normal(d0)
+    qrot = oracle.fwht(q) / np.sqrt(d0)
+    assert np.allclose(krot @ qrot, kd[0] @ q, rtol=0, atol=1e-12 * np.abs(kd[0] @ q).max())
+
+
+def _naive_rtn(x, bits):
+    """Per-token asymmetric RTN of the raw values (no rotation, no normalisation)."""
+    x = x.astype(np.float64)
+    mn = x.min(-1, keepdims=True)
+    mx = x.max(-1, keepdims=True)
+    s = (mx - mn) / ((1 << bits) - 1)
+    return np.rint((x - mn) / np.where(s > 0, s, 1)) * s + mn
+
+
+def test_kvarn_beats_naive_rtn_on_outlier_data():
+    # qualitative page claim: naive per-token RTN loses the normal channels
+    # to the outliers; rotation + normalisation keeps them
+    d0, B, n_kv, Hq, T = 128, 1, 2, 8, 512
+    k, v = synthetic.outlier_kv_host(0, B * n_kv, T, d0)
+    kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)
+    kq, vq = _quantize_pair(kt, vt)
+    Kd, _ = oracle.dequantize_tiles(kq["codes"], kq["meta"], d0, 4, True)
+    Vd, _ = oracle.dequantize_tiles(vq["codes"], vq["meta"], d0, 2, False)
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)  # noqa: E731
+    assert rel(Kd.reshape(K.shape), K) < rel(_naive_rtn(k, 4), K)
+    assert rel(Vd.reshape(V.shape), V) < rel(_naive_rtn(v, 2), V)
+    q = synthetic.query_host(3, B, Hq, d0)
+    ref = _sdpa_ref(q, K, V, n_kv)
+    o = oracle.decode_attention(q, kq["codes"], vq["codes"], kq["meta"], vq["meta"],
+                                n_kv_heads=n_kv, tiles_per_seq=T // 128)
+    naive = _sdpa_ref(q, _naive_rtn(k, 4), _naive_rtn(v, 2), n_kv)
+    assert rel(o, ref) < rel(naive, ref)

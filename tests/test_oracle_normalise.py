@@ -1,0 +1,203 @@
+"""Pins of the oracle's Sinkhorn-style log-space normalisation.
+
+Page: "KVarN Hadamard 旋转与方差归一化" (blog.hotdry.top), section
+"迭代方差归一化：Sinkhorn 式的动态校准" (column pass, row pass, repeat; usually
+3-5 iterations; factors kept for dequantisation), and the deep-dive page's
+Sinkhorn paragraph in "四個步驟".
+
+What is checked (none of it retypes the oracle's formula):
+  - after the final row pass every token row has population std exactly 1;
+  - the total-variance identity that any tile with unit row stds obeys:
+    mean_j sigma_j^2 = 1 + var_t(row mean) - var_j(column mean).  It ties the
+    column stds to the row and column means, so it fails if the std were
+    taken about zero instead of about the mean;
+  - when no token row carries a large mean, the columns are balanced: their
+    stds agree with their geometric mean g to 1e-2 at 5 iterations and
+    |g - 1| <= 2e-2 (a centred-std scaling cannot make every row and column
+    std 1 at once, so g is bounded rather than required to be 1);
+  - a tile with an outlier in channel 0 (which the all-ones Hadamard column
+    turns into a per-token offset) drifts instead: g grows well above 1,
+    exactly as the identity predicts from the row means;
+  - n_iters = 0 leaves the rotated tile untouched;
+  - scaling the input by a power of two changes no code and scales the
+    dequantised tile by the same power of two;
+  - permuting the tokens of a tile permutes the token factors and the codes;
+  - the degenerate tiles (all zero, constant) give their closed-form result.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_bit_token_amd import synthetic
+
+
+def _cfg1_tiles():
+    k, v = synthetic.outlier_kv_host(0, 1, 512, 128)
+    return synthetic.as_tiles(k), synthetic.as_tiles(v)
+
+
+def _popstd(a, axis):
+    return np.sqrt(((a - a.mean(axis=axis, keepdims=True)) ** 2).mean(axis=axis))
+
+
+def _stats(y):
+    rows = _popstd(y, 1)
+    cols = _popstd(y, 0)
+    g = np.exp(np.log(cols).mean())
+    return rows, cols, g
+
+
+def _check_identity(y):
+    rows, cols, _ = _stats(y)
+    assert np.allclose(rows, 1.0, rtol=0, atol=1e-12)
+    rm, cm = y.mean(1), y.mean(0)
+    lhs = (cols ** 2).mean()
+    rhs = 1.0 + rm.var() - cm.var()
+    assert abs(lhs - rhs) <= 1e-9 * max(1.0, lhs), (lhs, rhs)
+
+
+def _check_balance(y, n_iters):
+    _check_identity(y)
+    _, cols, g = _stats(y)
+    bal = np.abs(cols / g - 1).max()
+    if n_iters >= 5:
+        assert bal <= 1e-2, bal
+    assert abs(g - 1) <= 2e-2, g
+
+
+def _normalised(x16, n_iters):
+    xt = oracle.rotate_tile(x16)
+    lr, lc = oracle.normalise(xt, n_iters)
+    return xt * np.exp(-lr[:, None] - lc[None, :])
+
+
+@pytest.mark.parametrize("n_iters", [3, 5])
+def test_rows_unit_columns_balanced_cfg1(n_iters):
+    kt, vt = _cfg1_tiles()
+    for tiles in (kt, vt):
+        for x16 in tiles:
+            _check_balance(_normalised(x16, n_iters), n_iters)
+
+
+@pytest.mark.parametrize("d0", [64, 96, 256])
+def test_rows_unit_columns_balanced_other_dims(d0):
+    # seed 5 puts no outlier in channel 0 for any of these widths
+    k, v = synthetic.outlier_kv_host(5, 1, 256, d0, tok_frac=0.02)
+    for x16 in np.concatenate([synthetic.as_tiles(k), synthetic.as_tiles(v)]):
+        _check_balance(_normalised(x16, 5), 5)
+
+
+@pytest.mark.parametrize("d0", [64, 96])
+def test_channel0_outlier_drifts_as_identity_predicts(d0):
+    # seed 4 puts an outlier in channel 0 of V at both widths
+    _, v = synthetic.outlier_kv_host(4, 1, 256, d0)
+    for x16 in synthetic.as_tiles(v):
+        y = _normalised(x16, 5)
+        _check_identity(y)
+        _, _, g = _stats(y)
+        assert g > 1.2
+        assert y.mean(1).var() > 0.4
+
+
+@pytest.mark.parametrize("n_iters", [1, 2])
+def test_iteration_count_and_order_against_numpy_std(n_iters):
+    # One iteration = a column pass then a row pass, each dividing by numpy's
+    # population std (ddof=0) of the current values; the log-factors are the
+    # logs of the accumulated divisors.
+    kt, _ = _cfg1_tiles()
+    xt = oracle.rotate_tile(kt[2])
+    col = np.ones(xt.shape[1])
+    row = np.ones(xt.shape[0])
+    for _ in range(n_iters):
+        col = col * np.std(xt / row[:, None] / col[None, :], axis=0)
+        row = row * np.std(xt / row[:, None] / col[None, :], axis=1)
+    lr, lc = oracle.normalise(xt, n_iters)
+    assert np.allclose(np.exp(lc), col, rtol=1e-12, atol=0)
+    assert np.allclose(np.exp(lr), row, rtol=1e-12, atol=0)
+
+
+def test_more_iterations_improve_balance():
+    kt, _ = _cfg1_tiles()
+    xt = oracle.rotate_tile(kt[0])
+    bals = []
+    for n in (1, 3, 5):
+        lr, lc = oracle.normalise(xt, n)
+        y = xt * np.exp(-lr[:, None] - lc[None, :])
+        cols = _popstd(y, 0)
+        bals.append(np.abs(cols / np.exp(np.log(cols).mean()) - 1).max())
+    assert bals[0] > bals[1] > bals[2]
+
+
+def test_zero_iterations_is_rotation_only():
+    kt, _ = _cfg1_tiles()
+    q = oracle.quantize_tiles(kt[:1], 4, 0, True, diag=True)
+    xt = oracle.rotate_tile(kt[0])
+    assert np.array_equal(q["lr"][0], np.zeros(128))
+    assert np.array_equal(q["lc"][0], np.zeros(128))
+    assert np.array_equal(q["y"][0], xt)
+
+
+@pytest.mark.parametrize("is_key,bits", [(True, 4), (False, 2)])
+def test_power_of_two_scaling_invariance(is_key, bits):
+    kt, vt = _cfg1_tiles()
+    x = (kt if is_key else vt)[:2].astype(np.float64)
+    a = oracle.quantize_tiles(x.astype(np.float16), bits, 5, is_key)
+    b = oracle.quantize_tiles((x * 8.0).astype(np.float16), bits, 5, is_key)
+    assert np.array_equal(a["codes"], b["codes"])
+    da, _ = oracle.dequantize_tiles(a["codes"], a["meta"], 128, bits, is_key)
+    db, _ = oracle.dequantize_tiles(b["codes"], b["meta"], 128, bits, is_key)
+    scale = np.abs(da).max()
+    assert np.allclose(db, 8.0 * da, rtol=0, atol=3e-3 * 8.0 * scale)
+
+
+@pytest.mark.parametrize("is_key,bits", [(True, 4), (False, 2)])
+def test_token_permutation_equivariance(is_key, bits):
+    kt, vt = _cfg1_tiles()
+    x = (kt if is_key else vt)[1:2]
+    perm = np.random.default_rng(5).permutation(128)
+    a = oracle.quantize_tiles(x, bits, 5, is_key, diag=True)
+    b = oracle.quantize_tiles(x[:, perm], bits, 5, is_key, diag=True)
+    assert np.allclose(b["lr"][0], a["lr"][0][perm], rtol=0, atol=1e-12)
+    assert np.allclose(b["lc"][0], a["lc"][0], rtol=0, atol=1e-12)
+    ca = oracle.unpack(a["codes"][0], 128, bits, is_key)
+    cb = oracle.unpack(b["codes"][0], 128, bits, is_key)
+    assert np.array_equal(cb, ca[perm])
+
+
+@pytest.mark.parametrize("d0", [128, 96])
+def test_all_zero_tile(d0):
+    x = np.zeros((1, 128, d0), np.float16)
+    D = oracle.padded_dim(d0)
+    k = oracle.quantize_tiles(x, 4, 5, True)
+    v = oracle.quantize_tiles(x, 2, 5, False)
+    assert not k["codes"].any() and not v["codes"].any()
+    km, vm = k["meta"][0].astype(np.float64), v["meta"][0].astype(np.float64)
+    assert np.array_equal(km[:2 * D], np.zeros(2 * D)) and np.array_equal(km[2 * D:], np.ones(128))
+    assert np.array_equal(vm[:256], np.zeros(256)) and np.array_equal(vm[256:], np.ones(D))
+    o, _ = oracle.dequantize_tiles(k["codes"], k["meta"], d0, 4, True)
+    assert not o.any()
+
+
+def test_constant_tile_closed_form():
+    c = 1.5
+    D = 128
+    x = np.full((1, 128, D), c, np.float16)
+    q = oracle.quantize_tiles(x, 4, 5, True, diag=True)
+    # rotation: channel 0 holds c * sqrt(D), all others 0; every column is
+    # flat, so no column factor moves; each row (c sqrt(D), 0, ..., 0) has
+    # population std c sqrt(D) sqrt(D - 1) / D.
+    C = c * np.sqrt(D)
+    assert np.array_equal(q["lc"][0], np.zeros(D))
+    assert np.allclose(q["lr"][0], np.log(C * np.sqrt(D - 1) / D), rtol=0, atol=1e-12)
+    assert not q["codes"].any()                       # K: every column group is flat
+    sk, zk, rk = np.split(q["meta"][0].astype(np.float64), [D, 2 * D])
+    assert not sk.any() and not zk[1:].any()
+    assert np.isclose(zk[0] * rk[0], C, rtol=2e-3)
+    o, _ = oracle.dequantize_tiles(q["codes"], q["meta"], D, 4, True)
+    assert np.allclose(o, c, rtol=0, atol=4e-3)
+    # V: every row is (C', 0, ..., 0): channel 0 gets the top code, the rest 0
+    qv = oracle.quantize_tiles(x, 2, 5, False)
+    cv = oracle.unpack(qv["codes"][0], D, 2, False)
+    assert np.all(cv[:, 0] == 3) and not cv[:, 1:].any()
+    ov, _ = oracle.dequantize_tiles(qv["codes"], qv["meta"], D, 2, False)
+    assert np.allclose(ov, c, rtol=0, atol=4e-3)
