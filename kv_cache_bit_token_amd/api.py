@@ -1,0 +1,174 @@
+"""Python binding of libkvarn.so, same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind include/kvarn.h.  torch supplies device memory (outputs are allocated
+with torch on the inputs' device) and the stream (the current stream).  All
+tensors must be CUDA (ROCm) tensors; there is no CPU fallback.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+TILE = 128
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, fn, status):
+        lib = _lib.load()
+        msg = lib.kvarn_status_str(status).decode()
+        super().__init__("%s failed: %s (%s)" % (fn, _lib.STATUS.get(status, status), msg))
+        self.status = status
+
+
+def _check(fn, st):
+    if st != 0:
+        raise KvarnError(fn, st)
+
+
+def _params(head_dim, k_bits, v_bits, n_iters, tile_tokens=TILE):
+    return _lib.Params(int(head_dim), int(tile_tokens), int(k_bits), int(v_bits), int(n_iters))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (the KVarN path has no CPU fallback)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def get_layout(head_dim, k_bits=4, v_bits=2, n_iters=5):
+    """Per-tile sizes of the packed format (host only)."""
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, n_iters)
+    lay = _lib.TileLayout()
+    _check("kvarn_get_layout", lib.kvarn_get_layout(ctypes.byref(p), ctypes.byref(lay)))
+    return {"padded_dim": lay.padded_dim, "k_code_bytes": lay.k_code_bytes,
+            "v_code_bytes": lay.v_code_bytes, "k_meta_bytes": lay.k_meta_bytes,
+            "v_meta_bytes": lay.v_meta_bytes}
+
+
+def params_from_preset(preset, head_dim, n_iters=5):
+    """Parse e.g. 'kvarn_k4v2_g128' -> dict(head_dim, tile_tokens, k_bits, v_bits, n_iters)."""
+    lib = _lib.load()
+    p = _lib.Params()
+    _check("kvarn_params_from_preset",
+           lib.kvarn_params_from_preset(preset.encode(), int(head_dim), int(n_iters), ctypes.byref(p)))
+    return {"head_dim": p.head_dim, "tile_tokens": p.tile_tokens, "k_bits": p.k_bits,
+            "v_bits": p.v_bits, "n_iters": p.n_iters}
+
+
+def quantize_tiles(k, v, *, k_bits=4, v_bits=2, n_iters=5, out=None):
+    """Quantise fp16 K and V tiles.
+
+    k, v: torch.float16 GPU tensors whose trailing dims are [128, head_dim]
+    (all leading dims are tiles); either may be None to skip that tensor.
+    Returns (k_codes, v_codes, k_meta, v_meta): uint8 [n_tiles, code_bytes]
+    and float16 [n_tiles, meta_halves] (None for a skipped tensor).  `out`
+    may pass preallocated outputs in the same order.
+    """
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("nothing to quantise")
+    head_dim = ref.shape[-1]
+    n_tiles = ref.numel() // (TILE * head_dim)
+    for t, name in ((k, "k"), (v, "v")):
+        _need_gpu(t, name, torch.float16)
+        if t is not None and (t.shape[-2] != TILE or t.numel() != n_tiles * TILE * head_dim):
+            raise ValueError("%s must be [..., 128, head_dim] with the same tile count" % name)
+    lay = get_layout(head_dim, k_bits, v_bits, n_iters)
+    dev = ref.device
+    if out is None:
+        kc = torch.empty((n_tiles, lay["k_code_bytes"]), dtype=torch.uint8, device=dev) if k is not None else None
+        vc = torch.empty((n_tiles, lay["v_code_bytes"]), dtype=torch.uint8, device=dev) if v is not None else None
+        km = torch.empty((n_tiles, lay["k_meta_bytes"] // 2), dtype=torch.float16, device=dev) if k is not None else None
+        vm = torch.empty((n_tiles, lay["v_meta_bytes"] // 2), dtype=torch.float16, device=dev) if v is not None else None
+    else:
+        kc, vc, km, vm = out
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, n_iters)
+    st = lib.kvarn_quantize_tiles(ctypes.byref(p), n_tiles, _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                  _ptr(km), _ptr(vm), _stream(dev))
+    _check("kvarn_quantize_tiles", st)
+    return kc, vc, km, vm
+
+
+def dequantize_tiles(k_codes, v_codes, k_meta, v_meta, *, head_dim, k_bits=4, v_bits=2,
+                     out=None):
+    """Inverse of quantize_tiles -> (k, v) torch.float16 [n_tiles, 128, head_dim]."""
+    ref = k_codes if k_codes is not None else v_codes
+    n_tiles = ref.shape[0]
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need_gpu(t, name, torch.uint8)
+    for t, name in ((k_meta, "k_meta"), (v_meta, "v_meta")):
+        _need_gpu(t, name, torch.float16)
+    dev = ref.device
+    if out is None:
+        ko = torch.empty((n_tiles, TILE, head_dim), dtype=torch.float16, device=dev) if k_codes is not None else None
+        vo = torch.empty((n_tiles, TILE, head_dim), dtype=torch.float16, device=dev) if v_codes is not None else None
+    else:
+        ko, vo = out
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    st = lib.kvarn_dequantize_tiles(ctypes.byref(p), n_tiles, _ptr(k_codes), _ptr(v_codes),
+                                    _ptr(k_meta), _ptr(v_meta), _ptr(ko), _ptr(vo), _stream(dev))
+    _check("kvarn_dequantize_tiles", st)
+    return ko, vo
+
+
+def decode_attention_workspace(*, batch, n_q_heads, n_kv_heads, tiles_per_seq, head_dim,
+                               k_bits=4, v_bits=2):
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    nb = ctypes.c_size_t()
+    _check("kvarn_decode_attention_workspace",
+           lib.kvarn_decode_attention_workspace(ctypes.byref(p), int(batch), int(n_q_heads),
+                                                int(n_kv_heads), int(tiles_per_seq),
+                                                ctypes.byref(nb)))
+    return nb.value
+
+
+def decode_attention(q, k_codes, v_codes, k_meta, v_meta, *, n_kv_heads, tiles_per_seq,
+                     k_bits=4, v_bits=2, sm_scale=None, workspace=None, out=None):
+    """One decode step over the packed cache.
+
+    q: torch.float16 [batch, n_q_heads, head_dim]; cache tile i of (b, g) at
+    row (b * n_kv_heads + g) * tiles_per_seq + i of the code/meta tensors.
+    Returns float32 [batch, n_q_heads, head_dim].
+    """
+    _need_gpu(q, "q", torch.float16)
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need_gpu(t, name, torch.uint8)
+    for t, name in ((k_meta, "k_meta"), (v_meta, "v_meta")):
+        _need_gpu(t, name, torch.float16)
+    batch, hq, head_dim = q.shape
+    if sm_scale is None:
+        sm_scale = head_dim ** -0.5
+    nbytes = decode_attention_workspace(batch=batch, n_q_heads=hq, n_kv_heads=n_kv_heads,
+                                        tiles_per_seq=tiles_per_seq, head_dim=head_dim,
+                                        k_bits=k_bits, v_bits=v_bits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, hq, head_dim), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    st = lib.kvarn_decode_attention(ctypes.byref(p), batch, hq, int(n_kv_heads), int(tiles_per_seq),
+                                    _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_meta),
+                                    _ptr(v_meta), float(sm_scale), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("kvarn_decode_attention", st)
+    return out

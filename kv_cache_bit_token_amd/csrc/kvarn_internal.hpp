@@ -1,0 +1,63 @@
+// kvarn_internal.hpp -- launch interfaces between the C ABI (kvarn_abi.cpp)
+// and the kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+struct QuantArgs {
+    const uint16_t* k;  // [n_k][128][d0] fp16 bits
+    const uint16_t* v;  // [n_v][128][d0]
+    uint8_t* kc;
+    uint8_t* vc;
+    uint16_t* km;
+    uint16_t* vm;
+    int64_t n_k;        // tiles of K to process (0 = skip K)
+    int64_t n_v;        // tiles of V to process (0 = skip V)
+    int d0;
+    int n_iters;
+};
+
+struct DequantArgs {
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const uint16_t* km;
+    const uint16_t* vm;
+    uint16_t* ko;
+    uint16_t* vo;
+    int64_t n_k;
+    int64_t n_v;
+    int d0;
+};
+
+struct AttnArgs {
+    const uint16_t* q;   // [B][Hq][d0]
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const uint16_t* km;
+    const uint16_t* vm;
+    float* out;          // [B][Hq][d0]
+    float* ws;           // split-K partials
+    int batch;
+    int n_q_heads;
+    int n_kv_heads;
+    int tiles_per_seq;
+    int n_splits;        // splits per (b, g)
+    int tiles_per_split;
+    int d0;
+    float sm_scale;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, int D, int kb, int vb, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs& a, int D, int kb, int vb, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_t s);
+
+// Split-K plan of the decode attention for a shape (shared by the workspace
+// query and the launch, so both agree).
+void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
+                    int* tiles_per_split);
+size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_splits);
+
+}  // namespace kvarn

@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+libkvarn.so must load and export every function include/kvarn.h declares,
+and every argument error must come back as its status code from host-side
+validation, before anything touches a GPU.  Calls with valid arguments are
+limited to ones that launch nothing (n_tiles == 0, both tensors skipped).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_bit_token_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvarn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def P(head_dim=128, tile=128, kb=4, vb=2, it=5):
+    return _lib.Params(head_dim, tile, kb, vb, it)
+
+
+def test_layout_and_errors():
+    lib = _lib.load()
+    lay = _lib.TileLayout()
+    assert lib.kvarn_get_layout(ctypes.byref(P()), ctypes.byref(lay)) == 0
+    assert (lay.padded_dim, lay.k_code_bytes, lay.v_code_bytes, lay.k_meta_bytes,
+            lay.v_meta_bytes) == (128, 8192, 4096, 768, 768)
+    assert lib.kvarn_get_layout(ctypes.byref(P(96)), ctypes.byref(lay)) == 0 and lay.padded_dim == 128
+    assert lib.kvarn_get_layout(ctypes.byref(P(40)), ctypes.byref(lay)) == 0 and lay.padded_dim == 64
+    assert lib.kvarn_get_layout(ctypes.byref(P(256, kb=2, vb=4)), ctypes.byref(lay)) == 0
+    assert (lay.padded_dim, lay.k_code_bytes, lay.v_code_bytes) == (256, 8192, 16384)
+    cases = [
+        (None, 1), (P(head_dim=32), 2), (P(head_dim=264), 2), (P(head_dim=100), 2),
+        (P(tile=64), 3), (P(kb=3), 4), (P(vb=8), 4), (P(it=-1), 5), (P(it=17), 5),
+    ]
+    for p, want in cases:
+        arg = None if p is None else ctypes.byref(p)
+        assert lib.kvarn_get_layout(arg, ctypes.byref(lay)) == want, (p and (p.head_dim, p.tile_tokens))
+    assert lib.kvarn_get_layout(ctypes.byref(P()), None) == 1
+
+
+def test_preset_parser():
+    lib = _lib.load()
+    p = _lib.Params()
+    assert lib.kvarn_params_from_preset(b"kvarn_k4v2_g128", 128, 5, ctypes.byref(p)) == 0
+    assert (p.head_dim, p.tile_tokens, p.k_bits, p.v_bits, p.n_iters) == (128, 128, 4, 2, 5)
+    assert lib.kvarn_params_from_preset(b"kvarn_k2v2_g128", 96, 3, ctypes.byref(p)) == 0
+    assert (p.k_bits, p.v_bits, p.head_dim) == (2, 2, 96)
+    assert lib.kvarn_params_from_preset(b"kvarn_k4v2_g64", 128, 5, ctypes.byref(p)) == 3
+    assert lib.kvarn_params_from_preset(b"kvarn_k8v2_g128", 128, 5, ctypes.byref(p)) == 4
+    assert lib.kvarn_params_from_preset(b"fp8", 128, 5, ctypes.byref(p)) == 4
+    assert lib.kvarn_params_from_preset(b"kvarn_k4v2_g", 128, 5, ctypes.byref(p)) == 3
+    assert lib.kvarn_params_from_preset(None, 128, 5, ctypes.byref(p)) == 1
+    assert lib.kvarn_params_from_preset(b"kvarn_k4v2_g128", 128, 99, ctypes.byref(p)) == 5
+
+
+A = ctypes.c_void_p(0x10000)        # aligned, never dereferenced by these calls
+MIS = ctypes.c_void_p(0x10008)      # 8-byte aligned only
+
+
+def test_quantize_validation_without_launch():
+    lib = _lib.load()
+    q = lib.kvarn_quantize_tiles
+    ok = ctypes.byref(P())
+    # valid but launches nothing
+    assert q(ok, 0, A, A, A, A, A, A, None) == 0
+    assert q(ok, 5, None, None, None, None, None, None, None) == 0
+    # errors
+    assert q(None, 1, A, A, A, A, A, A, None) == 1
+    assert q(ctypes.byref(P(head_dim=30)), 1, A, A, A, A, A, A, None) == 2
+    assert q(ctypes.byref(P(tile=256)), 1, A, A, A, A, A, A, None) == 3
+    assert q(ctypes.byref(P(kb=1)), 1, A, A, A, A, A, A, None) == 4
+    assert q(ctypes.byref(P(it=40)), 1, A, A, A, A, A, A, None) == 5
+    assert q(ok, 1, A, A, None, A, A, A, None) == 1          # K set partly NULL
+    assert q(ok, 1, A, A, A, A, A, None, None) == 1          # V set partly NULL
+    assert q(ok, -1, A, A, A, A, A, A, None) == 6
+    assert q(ok, 1 << 40, A, A, A, A, A, A, None) == 6
+    assert q(ok, 1, MIS, A, A, A, A, A, None) == 7
+    assert q(ok, 1, A, A, A, A, A, MIS, None) == 7
+
+
+def test_dequantize_validation_without_launch():
+    lib = _lib.load()
+    d = lib.kvarn_dequantize_tiles
+    ok = ctypes.byref(P())
+    assert d(ok, 0, A, A, A, A, A, A, None) == 0
+    assert d(ok, 3, None, None, None, None, None, None, None) == 0
+    assert d(None, 1, A, A, A, A, A, A, None) == 1
+    assert d(ctypes.byref(P(vb=3)), 1, A, A, A, A, A, A, None) == 4
+    assert d(ok, 1, A, A, None, A, A, A, None) == 1
+    assert d(ok, -2, A, A, A, A, A, A, None) == 6
+    assert d(ok, 1, A, A, A, A, MIS, A, None) == 7
+
+
+def test_attention_validation_without_launch():
+    lib = _lib.load()
+    ws = lib.kvarn_decode_attention_workspace
+    nb = ctypes.c_size_t()
+    ok = ctypes.byref(P())
+    assert ws(ok, 64, 32, 8, 256, ctypes.byref(nb)) == 0 and nb.value > 0
+    need = nb.value
+    assert ws(ok, 64, 30, 8, 256, ctypes.byref(nb)) == 6      # 30 % 8 != 0
+    assert ws(ok, -1, 32, 8, 256, ctypes.byref(nb)) == 6
+    assert ws(ok, 1, 64, 2, 1, ctypes.byref(nb)) == 6         # group of 32 heads > 16
+    assert ws(ok, 64, 32, 8, 256, None) == 1
+    at = lib.kvarn_decode_attention
+    assert at(ok, 0, 32, 8, 256, A, A, A, A, A, 0.1, A, A, need, None) == 0   # empty batch
+    assert at(ok, 64, 32, 8, 256, None, A, A, A, A, 0.1, A, A, need, None) == 1
+    assert at(ok, 64, 32, 8, 256, A, A, A, A, A, 0.1, A, None, need, None) == 1
+    assert at(ok, 64, 32, 8, 256, A, A, A, A, A, 0.1, A, A, need - 4, None) == 8
+    assert at(ok, 64, 32, 8, 256, A, A, A, A, MIS, 0.1, A, A, need, None) == 7
+    assert at(ctypes.byref(P(head_dim=7)), 64, 32, 8, 256, A, A, A, A, A, 0.1, A, A, need, None) == 2
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(10):
+        assert lib.kvarn_status_str(code)
+    assert lib.kvarn_status_str(42) == b"unknown status"
+
+
+@pytest.mark.parametrize("name", ["quantize_tiles", "dequantize_tiles", "decode_attention"])
+def test_python_api_refuses_cpu_tensors(name):
+    import torch
+    import kv_cache_bit_token_amd as kv
+    x = torch.zeros(1, 128, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        if name == "quantize_tiles":
+            kv.quantize_tiles(x, x)
+        elif name == "dequantize_tiles":
+            c = torch.zeros(1, 8192, dtype=torch.uint8)
+            m = torch.zeros(1, 384, dtype=torch.float16)
+            kv.dequantize_tiles(c, c, m, m, head_dim=128)
+        else:
+            c = torch.zeros(1, 8192, dtype=torch.uint8)
+            m = torch.zeros(1, 384, dtype=torch.float16)
+            kv.decode_attention(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m,
+                                n_kv_heads=1, tiles_per_seq=1)

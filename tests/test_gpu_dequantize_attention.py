@@ -1,0 +1,100 @@
+"""GPU parity of kvarn_dequantize_tiles and kvarn_decode_attention.
+
+Both kernels read packed caches written by the oracle's quantiser (or drawn
+at random), never by the GPU quantiser, so every expected value comes from
+the oracle alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_bit_token_amd as kv
+import oracle
+from kv_cache_bit_token_amd import synthetic
+from parity import compare_attention, compare_dequant
+
+pytestmark = pytest.mark.gpu
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _oracle_cache(seed, heads, tokens, d0, kb=4, vb=2, n_iters=5):
+    k, v = synthetic.outlier_kv_host(seed, heads, tokens, d0)
+    kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)
+    qk = oracle.quantize_tiles(kt, kb, n_iters, True)
+    qv = oracle.quantize_tiles(vt, vb, n_iters, False)
+    return k, v, qk, qv
+
+
+def _gpu_dequant(qk, qv, d0, kb, vb):
+    ko, vo = kv.dequantize_tiles(_cuda(qk["codes"]), _cuda(qv["codes"]), _cuda(qk["meta"]),
+                                 _cuda(qv["meta"]), head_dim=d0, k_bits=kb, v_bits=vb)
+    torch.cuda.synchronize()
+    return ko.cpu().numpy(), vo.cpu().numpy()
+
+
+@pytest.mark.parametrize("d0,kb,vb", [(128, 4, 2), (128, 4, 4), (128, 2, 2), (128, 2, 4),
+                                      (64, 4, 2), (96, 4, 2), (256, 4, 2), (40, 4, 2),
+                                      (200, 4, 2)])
+def test_dequantize_oracle_packed(d0, kb, vb):
+    _, _, qk, qv = _oracle_cache(6, 2, 384, d0, kb, vb)
+    ko, vo = _gpu_dequant(qk, qv, d0, kb, vb)
+    rk, _ = oracle.dequantize_tiles(qk["codes"], qk["meta"], d0, kb, True)
+    rv, _ = oracle.dequantize_tiles(qv["codes"], qv["meta"], d0, vb, False)
+    print(compare_dequant(ko, rk), compare_dequant(vo, rv))
+
+
+@pytest.mark.parametrize("d0", [128, 64, 256])
+def test_dequantize_random_packed(d0):
+    rng = np.random.default_rng(d0)
+    n = 5
+    D = oracle.padded_dim(d0)
+    kc = rng.integers(0, 256, size=(n, oracle.code_bytes(D, 4)), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(n, oracle.code_bytes(D, 2)), dtype=np.uint8)
+    km = np.concatenate([rng.uniform(0.01, 2.0, (n, D)), rng.uniform(-10, 10, (n, D)),
+                         rng.uniform(0.1, 5.0, (n, 128))], axis=1).astype(np.float16)
+    vm = np.concatenate([rng.uniform(0.01, 2.0, (n, 128)), rng.uniform(-3, 3, (n, 128)),
+                         rng.uniform(0.1, 5.0, (n, D))], axis=1).astype(np.float16)
+    qk, qv = {"codes": kc, "meta": km}, {"codes": vc, "meta": vm}
+    ko, vo = _gpu_dequant(qk, qv, d0, 4, 2)
+    rk, _ = oracle.dequantize_tiles(kc, km, d0, 4, True)
+    rv, _ = oracle.dequantize_tiles(vc, vm, d0, 2, False)
+    print(compare_dequant(ko, rk), compare_dequant(vo, rv))
+
+
+def _attention_case(B, n_kv, Hq, T, d0, seed, kb=4, vb=2):
+    k, v, qk, qv = _oracle_cache(seed, B * n_kv, T, d0, kb, vb)
+    q = synthetic.query_host(seed, B, Hq, d0)
+    out = kv.decode_attention(_cuda(q), _cuda(qk["codes"]), _cuda(qv["codes"]), _cuda(qk["meta"]),
+                              _cuda(qv["meta"]), n_kv_heads=n_kv, tiles_per_seq=T // 128,
+                              k_bits=kb, v_bits=vb)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q, qk["codes"], qv["codes"], qk["meta"], qv["meta"],
+                                  n_kv_heads=n_kv, tiles_per_seq=T // 128, k_bits=kb, v_bits=vb)
+    return out.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("B,n_kv,Hq,T,d0", [(2, 2, 8, 512, 128), (1, 1, 1, 128, 128),
+                                            (2, 1, 8, 384, 128), (1, 2, 32, 256, 128),
+                                            (1, 2, 8, 512, 96), (2, 2, 4, 256, 64),
+                                            (1, 1, 4, 256, 256)])
+def test_attention_oracle_packed(B, n_kv, Hq, T, d0):
+    out, ref = _attention_case(B, n_kv, Hq, T, d0, seed=B * 100 + Hq + d0)
+    print(compare_attention(out, ref))
+
+
+def test_attention_other_presets():
+    for kb, vb in ((4, 4), (2, 2)):
+        out, ref = _attention_case(1, 2, 8, 256, 128, seed=3, kb=kb, vb=vb)
+        print(kb, vb, compare_attention(out, ref))
+
+
+def test_attention_empty_cache_is_zero():
+    q = _cuda(synthetic.query_host(0, 2, 8, 128))
+    c = torch.zeros((1, 16), dtype=torch.uint8, device="cuda")
+    m = torch.zeros((1, 8), dtype=torch.float16, device="cuda")
+    out = kv.decode_attention(q, c, c, m, m, n_kv_heads=2, tiles_per_seq=0)
+    torch.cuda.synchronize()
+    assert not out.cpu().numpy().any()

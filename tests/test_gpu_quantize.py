@@ -1,0 +1,118 @@
+"""GPU parity of kvarn_quantize_tiles against the oracle, element by element.
+
+Sizes the oracle finishes in seconds: the 512-token single-head workload of
+the first configuration (K4V2, 5 iterations), the other bit presets, iteration
+counts 0/1/3/5, head_dim 64 / 96 (padded) / 256 and the ragged widths 40, 72
+and 200 whose last channel block is partly padding, odd tile counts, the
+degenerate tiles, and tiles whose normalisation drifts (outlier in channel 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_bit_token_amd as kv
+import oracle
+from kv_cache_bit_token_amd import synthetic
+from parity import compare_codes, compare_meta
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(k16, v16, kb, vb, n_iters):
+    k = torch.from_numpy(np.ascontiguousarray(k16)).cuda() if k16 is not None else None
+    v = torch.from_numpy(np.ascontiguousarray(v16)).cuda() if v16 is not None else None
+    outs = kv.quantize_tiles(k, v, k_bits=kb, v_bits=vb, n_iters=n_iters)
+    torch.cuda.synchronize()
+    return [None if o is None else o.cpu().numpy() for o in outs]
+
+
+def check_pair(k16, v16, kb=4, vb=2, n_iters=5):
+    d0 = k16.shape[-1]
+    D = oracle.padded_dim(d0)
+    kc, vc, km, vm = _gpu_quant(k16, v16, kb, vb, n_iters)
+    qk = oracle.quantize_tiles(k16, kb, n_iters, True, diag=True)
+    qv = oracle.quantize_tiles(v16, vb, n_iters, False, diag=True)
+    stats = {
+        "k_codes": compare_codes(kc, qk, D, kb, True),
+        "v_codes": compare_codes(vc, qv, D, vb, False),
+        "k_meta": compare_meta(km, qk["meta"], D, True),
+        "v_meta": compare_meta(vm, qv["meta"], D, False),
+    }
+    print(stats)
+    return stats
+
+
+def _cfg1():
+    k, v = synthetic.outlier_kv_host(0, 1, 512, 128)
+    return synthetic.as_tiles(k), synthetic.as_tiles(v)
+
+
+def test_config1_k4v2_5iters():
+    kt, vt = _cfg1()
+    check_pair(kt, vt, 4, 2, 5)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (2, 2), (2, 4)])
+def test_other_bit_presets(kb, vb):
+    kt, vt = _cfg1()
+    check_pair(kt, vt, kb, vb, 5)
+
+
+@pytest.mark.parametrize("n_iters", [0, 1, 3, 16])
+def test_iteration_counts(n_iters):
+    kt, vt = _cfg1()
+    check_pair(kt, vt, 4, 2, n_iters)
+
+
+@pytest.mark.parametrize("d0", [64, 96, 256, 40, 72, 200])
+@pytest.mark.parametrize("n_iters", [3, 5])
+def test_head_dims(d0, n_iters):
+    k, v = synthetic.outlier_kv_host(5, 2, 384, d0)      # 6 tiles: 2 heads x 3
+    check_pair(synthetic.as_tiles(k), synthetic.as_tiles(v), 4, 2, n_iters)
+
+
+@pytest.mark.parametrize("d0", [64, 96])
+def test_channel0_outlier_tiles(d0):
+    # outlier in channel 0: the centred-std normalisation drifts on these tiles
+    k, v = synthetic.outlier_kv_host(4, 1, 512, d0)
+    check_pair(synthetic.as_tiles(k), synthetic.as_tiles(v), 4, 2, 5)
+
+
+def test_degenerate_tiles():
+    rng = np.random.default_rng(17)
+    tiles = []
+    tiles.append(np.zeros((128, 128)))                         # all zero
+    tiles.append(np.full((128, 128), 1.5))                     # constant
+    tiles.append(np.tile(rng.standard_normal(128), (128, 1)))  # identical tokens
+    t = rng.standard_normal((128, 128)); t[:, 7] = 0.0; tiles.append(t)   # a zero channel
+    t = rng.standard_normal((128, 128)); t[5] *= 3000.0; tiles.append(t)  # one huge token
+    t = rng.standard_normal((128, 128)) * 1e-3; tiles.append(t)           # tiny values
+    t = np.zeros((128, 128)); t[:, 0] = rng.standard_normal(128); tiles.append(t)  # one channel
+    x = np.stack(tiles).astype(np.float16)
+    check_pair(x, x[::-1].copy(), 4, 2, 5)
+
+
+def test_odd_tile_count_and_independence():
+    k, v = synthetic.outlier_kv_host(8, 7, 128, 128)           # 7 tiles
+    kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)
+    a = _gpu_quant(kt, vt, 4, 2, 5)
+    b = _gpu_quant(kt, vt, 4, 2, 5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)                            # run-to-run bitwise identical
+    kt2 = kt.copy()
+    kt2[3] = (kt2[3].astype(np.float32) * -0.5).astype(np.float16)
+    c = _gpu_quant(kt2, vt, 4, 2, 5)
+    for i in range(7):
+        same = np.array_equal(a[0][i], c[0][i]) and np.array_equal(a[2][i], c[2][i])
+        assert same == (i != 3)
+    assert np.array_equal(a[1], c[1]) and np.array_equal(a[3], c[3])
+
+
+def test_skipping_one_tensor():
+    kt, vt = _cfg1()
+    both = _gpu_quant(kt, vt, 4, 2, 5)
+    vonly = _gpu_quant(None, vt, 4, 2, 5)
+    konly = _gpu_quant(kt, None, 4, 2, 5)
+    assert vonly[0] is None and konly[1] is None
+    assert np.array_equal(both[1], vonly[1]) and np.array_equal(both[3], vonly[3])
+    assert np.array_equal(both[0], konly[0]) and np.array_equal(both[2], konly[2])
