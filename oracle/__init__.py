@@ -43,6 +43,7 @@ def _load():
         "oracle_fwht": (None, [_dp, _int]),
         "oracle_rotate_tile": (None, [_u16p, _int, _dp]),
         "oracle_normalise": (None, [_dp, _int, _int, _dp, _dp]),
+        "oracle_recentre": (None, [_dp, _dp, _int]),
         "oracle_rtn_group": (None, [_dp, _int, _int, _int, _dp, _dp, _u8p, _int, _dp]),
         "oracle_code_bytes": (_i64, [_int, _int]),
         "oracle_meta_halves": (_i64, [_int, _int]),
@@ -139,6 +140,14 @@ def normalise(xt, n_iters: int):
     lr = np.empty(TILE, np.float64)
     lc = np.empty(D, np.float64)
     _load().oracle_normalise(_ptr(xt, _dp), D, int(n_iters), _ptr(lr, _dp), _ptr(lc, _dp))
+    return lr, lc
+
+
+def recentre(lr, lc):
+    """Gauge step: move mean(lc) from the column to the row log-factors."""
+    lr = np.array(lr, dtype=np.float64, copy=True)
+    lc = np.array(lc, dtype=np.float64, copy=True)
+    _load().oracle_recentre(_ptr(lr, _dp), _ptr(lc, _dp), lc.shape[0])
     return lr, lc
 
 

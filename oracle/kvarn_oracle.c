@@ -37,6 +37,8 @@
  *     [deep] §四個步驟, Sinkhorn paragraph).
  *   - A group whose values are all equal (exact comparison) has no spread to
  *     normalise and keeps its factor.
+ *   - After the last iteration the mean column log-factor is moved into the
+ *     row factors (oracle_recentre); Y and the codes do not change.
  *   - K is quantised per channel (over the 128 tokens), V per token (over the
  *     D channels) ([hotdry] §非对称量化与尺度折叠; [deep] KEY/VALUE table).
  *   - Asymmetric RTN: zero point = group min, scale = (max-min)/(2^b-1),
@@ -217,6 +219,26 @@ void oracle_normalise(const double *xt, int D, int n_iters, double *lr, double *
     }
 }
 
+/* Gauge of the stored factors.  Y depends on lr[t] + lc[j] only, so adding a
+ * constant to every lr and subtracting it from every lc changes neither Y,
+ * nor the codes, nor any dequantised value.  The iteration can drift the two
+ * sets apart (column factors up, row factors down, without bound on some
+ * tiles), which would push the stored binary16 factors out of range even
+ * though the factors exist only to restore the original range on read
+ * ([hotdry] §迭代方差归一化, last paragraph).  After the last iteration the
+ * tile's mean column log-factor therefore moves into the row factors. */
+void oracle_recentre(double *lr, double *lc, int D)
+{
+    double c = 0.0;
+    for (int j = 0; j < D; ++j)
+        c += lc[j];
+    c /= D;
+    for (int j = 0; j < D; ++j)
+        lc[j] -= c;
+    for (int t = 0; t < TILE; ++t)
+        lr[t] += c;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Asymmetric round-to-nearest of one group ([deep] worked 2-bit example:   */
 /* range [min, max], 2^b levels, scale = (max - min)/(2^b - 1), code =       */
@@ -307,6 +329,7 @@ void oracle_quantize_tile(const uint16_t *x, int d0, int bits, int n_iters, int 
 
     oracle_rotate_tile(x, d0, xt);
     oracle_normalise(xt, D, n_iters, lr, lc);
+    oracle_recentre(lr, lc, D);
     for (int t = 0; t < TILE; ++t)
         for (int j = 0; j < D; ++j)
             y[(size_t)t * D + j] = xt[(size_t)t * D + j] * exp(-lr[t] - lc[j]);

@@ -24,6 +24,8 @@ What is checked (none of it retypes the oracle's formula):
   - permuting the tokens of a tile permutes the token factors and the codes;
   - the degenerate tiles (all zero, constant) give their closed-form result.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -201,3 +203,51 @@ def test_constant_tile_closed_form():
     assert np.all(cv[:, 0] == 3) and not cv[:, 1:].any()
     ov, _ = oracle.dequantize_tiles(qv["codes"], qv["meta"], D, 2, False)
     assert np.allclose(ov, c, rtol=0, atol=4e-3)
+
+
+def test_recentre_moves_only_the_gauge():
+    rng = np.random.default_rng(11)
+    lr, lc = rng.normal(-3, 1, 128), rng.normal(5, 1, 128)
+    r2, c2 = oracle.recentre(lr, lc)
+    assert abs(c2.mean()) <= 1e-12
+    assert np.allclose(r2[:, None] + c2[None, :], lr[:, None] + lc[None, :], rtol=0, atol=1e-12)
+
+
+def test_quantize_uses_recentred_factors_without_changing_y():
+    kt, _ = _cfg1_tiles()
+    q = oracle.quantize_tiles(kt[:2], 4, 5, True, diag=True)
+    for i in range(2):
+        xt = oracle.rotate_tile(kt[i])
+        lr, lc = oracle.normalise(xt, 5)
+        assert abs(q["lc"][i].mean()) <= 1e-12
+        y_plain = xt * np.exp(-lr[:, None] - lc[None, :])
+        assert np.allclose(q["y"][i], y_plain, rtol=1e-12, atol=1e-300)
+
+
+GOLDEN_RUNAWAY = os.path.join(os.path.dirname(__file__), "golden", "runaway_tiles.npz")
+
+
+def test_runaway_tiles_store_finite_factors():
+    # tests/golden/runaway_tiles.txt: channel-0 outlier tiles whose factors
+    # drift apart; without the gauge step exp(lc) leaves the fp16 range
+    d = np.load(GOLDEN_RUNAWAY)
+    for x16, is_key in zip(d["x"], d["is_key"]):
+        xt = oracle.rotate_tile(x16)
+        lr, lc = oracle.normalise(xt, 5)
+        y = xt * np.exp(-lr[:, None] - lc[None, :])
+        if is_key:
+            plain = np.exp(lc) * (y.max(0) - y.min(0)).max()
+            assert np.abs(np.exp(lc)[None, :] * y.min(0)).max() > 65504 or plain > 65504
+        else:
+            assert np.exp(lc).max() > 65504
+        bits = 4 if is_key else 2
+        q = oracle.quantize_tiles(x16[None], bits, 5, bool(is_key), diag=True)
+        assert np.isfinite(q["meta"].astype(np.float64)).all()
+        o, _ = oracle.dequantize_tiles(q["codes"], q["meta"], 128, bits, bool(is_key))
+        assert np.isfinite(o).all()
+        # the rows the drift inflates widen every K column's range: the
+        # per-element bound still holds (s/2 in the normalised domain)
+        c = oracle.unpack(q["codes"][0], 128, bits, bool(is_key)).astype(np.float64)
+        ss = q["s"][0][None, :] if is_key else q["s"][0][:, None]
+        zz = q["z"][0][None, :] if is_key else q["z"][0][:, None]
+        assert np.all(np.abs(q["y"][0] - (c * ss + zz)) <= ss / 2 * (1 + 1e-12))
