@@ -8,10 +8,14 @@
 //
 // Everything runs in the rotated domain; nothing is dequantised to memory:
 //   qh = H q / sqrt(D)                       (once per (b, head), zero-padded)
-//   s_t = sm_scale * RK_t * (sum_j (qh_j SK_j) code_tj + sum_j qh_j ZK_j)
+//   s_t = sm_scale * RK_t * (sum_j (qh_j SK_j) (code_tj - mk) + sum_j qh_j (ZK_j + mk SK_j))
 //   online softmax over the tiles of a split
-//   acc_j = sum_t p_t CV_j (SV_t code_tj + ZV_t)
+//   acc_j = CV_j (sum_t p_t SV_t (code_tj - mv) + sum_t p_t (ZV_t + mv SV_t))
 //   o = H (acc / l) / sqrt(D), first head_dim channels      (combine kernel)
+// mk = (2^k_bits - 1)/2 and mv = (2^v_bits - 1)/2 centre the codes: ZK is the
+// group minimum, so sum_j qh_j SK_j code_tj and sum_j qh_j ZK_j are large
+// and of opposite sign; centred, neither term carries the cancellation and
+// the fp32 score keeps its accuracy when the scores are large.
 // Split-K: each workgroup owns one (b, KV head, split) and all the query
 // heads of that KV head's GQA group; a combine kernel merges the splits'
 // (max, sum, acc) partials and applies the inverse rotation.
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
     constexpr int KCB = TILE * D * KB / 8, VCB = TILE * D * VB / 8;
     constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
     constexpr uint32_t KMASK = (1u << KB) - 1, VMASK = (1u << VB) - 1;
+    constexpr float MK = 0.5f * (float)KMASK, MV = 0.5f * (float)VMASK;
     constexpr int GMAX = 16;
     __shared__ float qrot[GMAX * D];
     __shared__ float qs[GMAX * D];
@@ -123,7 +128,9 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
         for (int k = tid; k < G * D; k += ATT_THREADS) qs[k] = qrot[k] * h2f_bits(kmeta[k % D]);
         if (tid < G) {
             float z = 0.0f;
-            for (int j = 0; j < D; ++j) z = __builtin_fmaf(qrot[tid * D + j], h2f_bits(kmeta[D + j]), z);
+            for (int j = 0; j < D; ++j)
+                z = __builtin_fmaf(qrot[tid * D + j],
+                                   __builtin_fmaf(MK, h2f_bits(kmeta[j]), h2f_bits(kmeta[D + j])), z);
             qz[tid] = z;
         }
         __syncthreads();
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
             for (int j = 0; j < D; ++j) {
                 const int64_t e = (int64_t)t * D + j;
                 const uint32_t c = (kcode[(e * KB) >> 3] >> ((e * KB) & 7)) & KMASK;
-                s = __builtin_fmaf(qs[hh * D + j], (float)c, s);
+                s = __builtin_fmaf(qs[hh * D + j], (float)c - MK, s);
             }
             sc[k] = a.sm_scale * h2f_bits(kmeta[2 * D + t]) * (s + qz[hh]);
         }
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
                 float l = p0 + p1;
                 const float sv0 = h2f_bits(vmeta[lane]), sv1 = h2f_bits(vmeta[64 + lane]);
                 const float zv0 = h2f_bits(vmeta[TILE + lane]), zv1 = h2f_bits(vmeta[TILE + 64 + lane]);
-                float z = p0 * zv0 + p1 * zv1;
+                float z = p0 * __builtin_fmaf(MV, sv0, zv0) + p1 * __builtin_fmaf(MV, sv1, zv1);
                 for (int o = 32; o > 0; o >>= 1) { l += __shfl_xor(l, o); z += __shfl_xor(z, o); }
                 sc[hh * TILE + lane] = p0 * sv0;
                 sc[hh * TILE + 64 + lane] = p1 * sv1;
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
                 for (int t = 0; t < TILE; ++t) {
                     const int64_t e = (int64_t)j * TILE + t;
                     const uint32_t c = (vcode[(e * VB) >> 3] >> ((e * VB) & 7)) & VMASK;
-                    s = __builtin_fmaf(sc[hh * TILE + t], (float)c, s);
+                    s = __builtin_fmaf(sc[hh * TILE + t], (float)c - MV, s);
                 }
                 acc[r] = acc[r] * alpha[hh] + h2f_bits(vmeta[2 * TILE + j]) * (s + pz[hh]);
             }

@@ -164,6 +164,28 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         }
     }
 
+    // ---------------- gauge of the stored factors ----------------
+    // The normalised tile depends on l_r[t] + l_c[c] only.  The mean column
+    // log-factor is moved into the row factors (G = geometric mean of the
+    // column factors) so the stored fp16 factors stay in range even when the
+    // iteration drifts the two sets apart.  Codes are unaffected; only the
+    // stored SK/ZK/RK (K) and SV/ZV/CV (V) see G.
+    float* gsum = lds + 66 * D;
+    float G, invG;
+    {
+        float s = logf(Cp * rsqrtD);   // both lanes of a position: the sum is 2x
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        if ((tid & 63) == 0) gsum[tid >> 6] = s;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) tot += gsum[w];
+        const float mean_lc = tot * (0.5f / D);
+        G = expf(mean_lc);
+        invG = expf(-mean_lc);
+    }
+
     // ---------------- quantisation parameters ----------------
     uint8_t* cimg = reinterpret_cast<uint8_t*>(lds);                  // packed code image
     uint16_t* mimg = reinterpret_cast<uint16_t*>(lds + CODE_BYTES / 4);  // meta image
@@ -217,12 +239,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         // meta: SK, ZK by the reducers (rotated channel index), RK by lane cb == 0
         if (rh == 0) {
             const int k = 16 * N::nu(rp >> 4) + (rp & 15);
-            mimg[k] = f2h_bits(sk * rsqrtD);
-            mimg[D + k] = f2h_bits(zk * rsqrtD);
+            mimg[k] = f2h_bits(sk * rsqrtD * invG);
+            mimg[D + k] = f2h_bits(zk * rsqrtD * invG);
         }
         if (cb == 0) {
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) mimg[2 * D + 4 * tb + i] = f2h_bits(Rt[i]);
+            for (int i = 0; i < TPL; ++i) mimg[2 * D + 4 * tb + i] = f2h_bits(Rt[i] * G);
         }
     } else {
         // V: one group per token, over the D channels: values v = x * b[c]
@@ -257,13 +279,13 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         if (cb == 0) {
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                mimg[4 * tb + i] = f2h_bits(sv[i]);
-                mimg[TILE + 4 * tb + i] = f2h_bits(zv[i]);
+                mimg[4 * tb + i] = f2h_bits(sv[i] * G);
+                mimg[TILE + 4 * tb + i] = f2h_bits(zv[i] * G);
             }
         }
         if (rh == 0) {
             const int k = 16 * N::nu(rp >> 4) + (rp & 15);
-            mimg[2 * TILE + k] = f2h_bits(Cp * rsqrtD);
+            mimg[2 * TILE + k] = f2h_bits(Cp * rsqrtD * invG);
         }
     }
 
@@ -317,9 +339,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
 }
 
 // LDS floats needed: part [32][D] + colv/colv2 [2][D] + the K max buffer
-// [32][D]; the code and meta images reuse the front.
+// [32][D] + 16 gauge partials; the code and meta images reuse the front.
 template <int D>
-constexpr int quant_lds_floats() { return 32 * D + 2 * D + 32 * D; }
+constexpr int quant_lds_floats() { return 32 * D + 2 * D + 32 * D + 16; }
 
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {

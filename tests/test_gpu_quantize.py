@@ -116,3 +116,13 @@ def test_skipping_one_tensor():
     assert vonly[0] is None and konly[1] is None
     assert np.array_equal(both[1], vonly[1]) and np.array_equal(both[3], vonly[3])
     assert np.array_equal(both[0], konly[0]) and np.array_equal(both[2], konly[2])
+
+
+def test_runaway_tiles():
+    # channel-0 outlier tiles whose factors drift apart (tests/golden/runaway_tiles.txt)
+    import os
+    d = np.load(os.path.join(os.path.dirname(__file__), "golden", "runaway_tiles.npz"))
+    x = d["x"]
+    kc, vc, km, vm = _gpu_quant(x, x, 4, 2, 5)
+    assert np.isfinite(km.astype(np.float64)).all() and np.isfinite(vm.astype(np.float64)).all()
+    check_pair(x, x, 4, 2, 5)
