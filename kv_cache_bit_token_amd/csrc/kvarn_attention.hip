@@ -6,33 +6,53 @@
 // so q.k is unchanged; hotdry page "非对称量化与尺度折叠": per-channel K
 // scales, per-token V scales, folded back on read).
 //
-// Everything runs in the rotated domain; nothing is dequantised to memory:
-//   qh = H q / sqrt(D)                       (once per (b, head), zero-padded)
-//   s_t = sm_scale * RK_t * (sum_j (qh_j SK_j) (code_tj - mk) + sum_j qh_j (ZK_j + mk SK_j))
+// Everything runs in the rotated domain; nothing is dequantised to memory.
+// With mk = 2^(k_bits-1), mv = 2^(v_bits-1):
+//   qh  = H q / sqrt(D)                          once per (b, query head)
+//   s_t = sm * RK_t * ( sum_j (qh_j SK_j)(code_tj - mk) + sum_j qh_j (ZK_j + mk SK_j) )
 //   online softmax over the tiles of a split
-//   acc_j = CV_j (sum_t p_t SV_t (code_tj - mv) + sum_t p_t (ZV_t + mv SV_t))
+//   acc_j = CV_j * ( sum_t (p_t SV_t)(code_tj - mv) + sum_t p_t (ZV_t + mv SV_t) )
 //   o = H (acc / l) / sqrt(D), first head_dim channels      (combine kernel)
-// mk = (2^k_bits - 1)/2 and mv = (2^v_bits - 1)/2 centre the codes: ZK is the
-// group minimum, so sum_j qh_j SK_j code_tj and sum_j qh_j ZK_j are large
-// and of opposite sign; centred, neither term carries the cancellation and
-// the fp32 score keeps its accuracy when the scores are large.
-// Split-K: each workgroup owns one (b, KV head, split) and all the query
-// heads of that KV head's GQA group; a combine kernel merges the splits'
-// (max, sum, acc) partials and applies the inverse rotation.
+// Centring the codes keeps both terms of each sum small (ZK is the group
+// minimum, so the uncentred terms would be large and of opposite sign).
+//
+// Matrix cores.  Both contractions run on v_mfma_f32_16x16x16_f16:
+//   q.K^T : A = codes (16 tokens x 16 channels), B = q' (16 channels x the
+//           GQA group's query heads, padded to 16), C = scores;
+//   p.V   : A = p' (query heads x 16 tokens), B = codes (16 tokens x 16
+//           channels), C = partial outputs.
+// Codes become exact fp16 values (c - 2^(b-1)) with a magic-number unpack;
+// q' = qh * SK and p' = p * SV are fp32 values split into fp16 hi + lo
+// parts (each scaled by a power of two per tile), so each product is exact
+// and the fp32 accumulation keeps fp32 accuracy.  The contraction axis is
+// permuted so every lane reads one contiguous run of packed codes: the K
+// row chunk of its token (16 bytes at K4, D = 128) and the V row chunk of
+// its channel (8 bytes at V2); the same permutation orders q' and p'.
+//
+// Work split: each wavefront owns one split (a run of tiles) of one
+// (b, KV head) and every query head of that head's GQA group; waves never
+// synchronise with each other.  Per tile, small per-wave LDS images move
+// q', the scores, p' and the p.V results between the matrix-core layouts and
+// dense layouts in which all 64 lanes do the softmax and the updates.  A
+// combine kernel merges the splits' (max, sum, acc) and undoes the rotation.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 
 namespace kvarn {
 
-constexpr int ATT_THREADS = 256;
-constexpr int kTargetBlocks = 2048;   // enough workgroups to fill 256 CUs several times
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTargetWaves = 8192;   // splits in flight: 8 waves per SIMD on 256 CUs
+constexpr float kLog2e = 1.4426950408889634f;
 
 void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
                     int* tiles_per_split) {
     const int64_t pairs = (int64_t)batch * n_kv_heads;
     int ns = 1;
     if (pairs > 0 && tiles_per_seq > 0) {
-        int64_t want = (kTargetBlocks + pairs - 1) / pairs;
+        int64_t want = (kTargetWaves + pairs - 1) / pairs;
         if (want > tiles_per_seq) want = tiles_per_seq;
         if (want < 1) want = 1;
         ns = (int)want;
@@ -47,8 +67,445 @@ size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_splits) 
     return (size_t)batch * n_q_heads * n_splits * (D + 2) * sizeof(float);
 }
 
-// In-LDS Walsh-Hadamard transform of `rows` vectors of length D (natural
-// order), scaled by 1/sqrt(D).
+// ---- b-bit codes -> exact fp16 (code - 2^(b-1)) -----------------------------
+// A packed dword holds N = 32/b codes.  Pair k takes codes k and k + N/2 (bits
+// b*k and b*k + 16) into the two halves of a dword: shifted into the fp16
+// mantissa under a magic exponent (16 + c for b = 4, 4 + c for b = 2), then
+// the magic and the centre are subtracted with one packed fp16 add.
+template <int B> struct Codes;
+template <> struct Codes<4> {
+    static constexpr int N = 8, TB = 6;
+    static constexpr uint32_t MASK = 0x03C003C0u, MAGIC = 0x4C004C00u;
+    static constexpr float SUB = 24.0f, MID = 8.0f;
+};
+template <> struct Codes<2> {
+    static constexpr int N = 16, TB = 8;
+    static constexpr uint32_t MASK = 0x03000300u, MAGIC = 0x44004400u;
+    static constexpr float SUB = 6.0f, MID = 2.0f;
+};
+
+template <int B>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int k) {
+    using C = Codes<B>;
+    const int sh = C::TB - B * k;
+    uint32_t x = sh >= 0 ? (w << sh) : (w >> (-sh));
+    x = (x & C::MASK) | C::MAGIC;
+    h2_t v = __builtin_bit_cast(h2_t, x);
+    v = v - (h2_t){(_Float16)C::SUB, (_Float16)C::SUB};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Matrix operand kb (4 fp16 values) out of a lane's run of packed dwords.
+// Operand kb uses dword d = kb / (N/4) and pairs 2*k2, 2*k2 + 1 (k2 = kb mod
+// N/4); element e holds code 2*k2 + (e >> 1) + (N/2)*(e & 1) of that dword.
+template <int B, int NW>
+__device__ __forceinline__ h4_t code_operand(const uint32_t (&w)[NW], int kb) {
+    constexpr int Q = Codes<B>::N / 4;
+    const int d = kb / Q, k2 = kb % Q;
+    const uint32_t lo = code_pair<B>(w[d], 2 * k2);
+    const uint32_t hi = code_pair<B>(w[d], 2 * k2 + 1);
+    return __builtin_bit_cast(h4_t, make_uint2(lo, hi));
+}
+
+// Runs of a dense task that covers operands kbase, kbase + 1 (kbase even) of a
+// lane group: the 8 elements are run0 + 0..3 and run1 + 0..3, stored
+// interleaved [r0_0, r1_0, r0_1, r1_1, r0_2, r1_2, r0_3, r1_3].
+template <int B>
+__device__ __forceinline__ int run0_of(int group_base, int kbase) {
+    constexpr int N = Codes<B>::N, Q = N / 4;
+    return group_base + N * (kbase / Q) + 2 * (kbase % Q);
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// reductions over aligned groups of W lanes (W = 8, 16, 32)
+template <int W>
+__device__ __forceinline__ float grp_sum(float v) {
+    v += dpp<DPP_XOR1>(v);
+    v += dpp<DPP_XOR2>(v);
+    v += dpp<DPP_HMIR>(v);
+    if constexpr (W >= 16) v += dpp<DPP_ROR8>(v);
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float grp_max(float v) {
+    v = fmaxf(v, dpp<DPP_XOR1>(v));
+    v = fmaxf(v, dpp<DPP_XOR2>(v));
+    v = fmaxf(v, dpp<DPP_HMIR>(v));
+    if constexpr (W >= 16) v = fmaxf(v, dpp<DPP_ROR8>(v));
+    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    return v;
+}
+
+// power-of-two scale s with max * s < 2^10 (1 for max == 0)
+__device__ __forceinline__ float pow2_scale(float mx) {
+    if (!(mx > 0.0f)) return 1.0f;
+    int e;
+    (void)frexpf(mx, &e);          // mx = m * 2^e, m in [0.5, 1)
+    return ldexpf(1.0f, 10 - e);
+}
+
+__device__ __forceinline__ void split_hi_lo(float x, _Float16& hi, _Float16& lo) {
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
+
+// Per-wave LDS layout (bytes), for GQA group size G (padded to GP = 4k).
+template <int D>
+struct AttnLds {
+    static constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
+    static constexpr int NKB = D / 16;
+    __host__ __device__ static int kmeta(int) { return 0; }
+    __host__ __device__ static int vmeta(int) { return 2 * KMH; }
+    __host__ __device__ static int bq(int) { return 2 * KMH + 2 * VMH; }
+    __host__ __device__ static int sc(int G) { return bq(G) + 64 * G * NKB; }
+    __host__ __device__ static int pa(int G) { return sc(G) + 512 * G; }
+    __host__ __device__ static int pvc(int G) { return pa(G) + 512 * G; }
+    __host__ __device__ static int stats(int G) { return pvc(G) + 4 * D * ((G + 3) & ~3); }
+    __host__ __device__ static int bytes(int G) { return stats(G) + 16 * G + 16; }
+};
+
+template <int D, int KB, int VB, int GMAX>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+    using L = AttnLds<D>;
+    constexpr int NKB = D / 16;                 // q.K^T operands per M-block (channels)
+    constexpr int NVB = TILE / 16;              // p.V operands per N-block (tokens)
+    constexpr int KROW = D * KB / 8;            // packed bytes of one token's K row
+    constexpr int VROW = TILE * VB / 8;         // packed bytes of one channel's V row
+    constexpr int KW = KROW / 16;               // dwords of a lane group's K chunk
+    constexpr int VW = VROW / 16;               // dwords of a lane group's V chunk
+    constexpr int KCB = TILE * KROW, VCB = D * VROW;
+    constexpr int QT = D / 8;                   // dense tasks per query (channels)
+    constexpr int QTMAX = (GMAX * QT + 63) / 64;
+    constexpr int STMAX = (GMAX * 16 + 63) / 64;
+    constexpr int CPL_E = D / 64;               // epilogue channels per lane
+    constexpr float MK = Codes<KB>::MID, MV = Codes<VB>::MID;
+
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wpb = blockDim.x >> 6;
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const int GP = (G + 3) & ~3;
+    const int sgroups = (a.n_splits + wpb - 1) / wpb;
+    const int bg = blockIdx.x / sgroups;
+    const int split = (blockIdx.x % sgroups) * wpb + wave;
+    if (split >= a.n_splits) return;
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int t0 = split * a.tiles_per_split;
+    const int t1 = min(t0 + a.tiles_per_split, a.tiles_per_seq);
+
+    uint8_t* lds = smem + (size_t)wave * L::bytes(G);
+    uint16_t* kmeta = reinterpret_cast<uint16_t*>(lds + L::kmeta(G));
+    uint16_t* vmeta = reinterpret_cast<uint16_t*>(lds + L::vmeta(G));
+    uint8_t* bqimg = lds + L::bq(G);
+    float* sc = reinterpret_cast<float*>(lds + L::sc(G));
+    uint8_t* paimg = lds + L::pa(G);
+    float* pvc = reinterpret_cast<float*>(lds + L::pvc(G));
+    float* st = reinterpret_cast<float*>(lds + L::stats(G));
+    float* st_qz = st;              // [G] zero-point term of the scores
+    float* st_iq = st + G;          // [G] 1 / q' scale
+    float* st_al = st + 2 * G;      // [G] softmax rescale of this tile
+    float* st_pz = st + 3 * G;      // [G] zero-point term of p.V
+    float* st_ip = st + 4 * G;      // [1] 1 / p' scale
+
+    const int mrow = lane & 15;     // MFMA row / column index of this lane
+    const int mgrp = lane >> 4;     // MFMA k-group of this lane
+
+    // ---- rotated queries, held by the dense q'-build tasks ----
+    // task t: query n = t / QT; lane group gq = (t % QT) / (NKB / 2); pair pr
+    float qh[QTMAX][8];
+    {
+        float* tmp = sc;   // [G][D] scratch before the tile loop
+        for (int k = lane; k < G * D; k += 64) {
+            const int n = k / D, j = k % D;
+            const int h = g * G + n;
+            tmp[k] = (j < a.d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + h) * a.d0 + j]) : 0.0f;
+        }
+        wave_sync();
+        // in-LDS Walsh-Hadamard transform of each query row
+        for (int hs = 1; hs < D; hs <<= 1) {
+            for (int k = lane; k < G * D / 2; k += 64) {
+                const int r = k / (D / 2), p = k % (D / 2);
+                const int lo = (p / hs) * 2 * hs + (p % hs), hi = lo + hs;
+                const float x = tmp[r * D + lo], y = tmp[r * D + hi];
+                tmp[r * D + lo] = x + y;
+                tmp[r * D + hi] = x - y;
+            }
+            wave_sync();
+        }
+        const float rs = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+        for (int r = 0; r < QTMAX; ++r) {
+            const int t = lane + 64 * r;
+            const int n = t / QT, rem = t % QT;
+            const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
+            const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qh[r][e] = (n < G) ? tmp[n * D + r0 + e] * rs : 0.0f;
+                qh[r][4 + e] = (n < G) ? tmp[n * D + r1 + e] * rs : 0.0f;
+            }
+        }
+        wave_sync();
+    }
+
+    // softmax state of the dense score tasks (task t: query t / 16)
+    float m_run[STMAX], l_run[STMAX];
+#pragma unroll
+    for (int r = 0; r < STMAX; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
+    // dense accumulator: channel lane + 64 * r, query n
+    float acc[CPL_E][GMAX];
+#pragma unroll
+    for (int r = 0; r < CPL_E; ++r)
+#pragma unroll
+        for (int n = 0; n < GMAX; ++n) acc[r][n] = 0.0f;
+
+    // MFMA operands built from the per-tile images (zero rows for n >= G)
+    h4_t bq_hi[NKB], bq_lo[NKB], pa_hi[NVB], pa_lo[NVB];
+#pragma unroll
+    for (int k = 0; k < NKB; ++k) { bq_hi[k] = (h4_t){0, 0, 0, 0}; bq_lo[k] = bq_hi[k]; }
+#pragma unroll
+    for (int k = 0; k < NVB; ++k) { pa_hi[k] = (h4_t){0, 0, 0, 0}; pa_lo[k] = pa_hi[k]; }
+
+    for (int ti = t0; ti < t1; ++ti) {
+        const int64_t tile = (int64_t)bg * a.tiles_per_seq + ti;
+        const uint8_t* kc = a.kc + tile * KCB;
+        const uint8_t* vc = a.vc + tile * VCB;
+
+        // ---- issue the tile's code loads (one contiguous run per lane) ----
+        uint32_t kw[TILE / 16][KW];   // 8 M-blocks of 16 tokens
+#pragma unroll
+        for (int mb = 0; mb < TILE / 16; ++mb) {
+            const uint8_t* p = kc + (size_t)(16 * mb + mrow) * KROW + mgrp * (KROW / 4);
+            if constexpr (KW >= 4) {
+#pragma unroll
+                for (int w = 0; w < KW; w += 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(p + 4 * w);
+                    kw[mb][w] = v.x; kw[mb][w + 1] = v.y; kw[mb][w + 2] = v.z; kw[mb][w + 3] = v.w;
+                }
+            } else if constexpr (KW == 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                kw[mb][0] = v.x; kw[mb][1] = v.y;
+            } else {
+                kw[mb][0] = *reinterpret_cast<const uint32_t*>(p);
+            }
+        }
+        uint32_t vw[NKB][VW];   // D/16 N-blocks of 16 channels
+#pragma unroll
+        for (int nb = 0; nb < NKB; ++nb) {
+            const uint8_t* p = vc + (size_t)(16 * nb + mrow) * VROW + mgrp * (VROW / 4);
+            if constexpr (VW == 4) {
+                const uint4 v = *reinterpret_cast<const uint4*>(p);
+                vw[nb][0] = v.x; vw[nb][1] = v.y; vw[nb][2] = v.z; vw[nb][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                vw[nb][0] = v.x; vw[nb][1] = v.y;
+            }
+        }
+        // ---- meta of the tile into the wave's LDS ----
+        {
+            const uint4* km = reinterpret_cast<const uint4*>(a.km + tile * L::KMH);
+            const uint4* vm = reinterpret_cast<const uint4*>(a.vm + tile * L::VMH);
+            constexpr int KC = 2 * L::KMH / 16, VC = 2 * L::VMH / 16;
+            for (int k = lane; k < KC + VC; k += 64) {
+                if (k < KC) reinterpret_cast<uint4*>(kmeta)[k] = km[k];
+                else reinterpret_cast<uint4*>(vmeta)[k - KC] = vm[k - KC];
+            }
+        }
+        wave_sync();
+
+        // ---- q' = qh * SK (hi/lo, scaled), zero-point term ----
+#pragma unroll
+        for (int r = 0; r < QTMAX; ++r) {
+            const int t = lane + 64 * r;
+            const int n = t / QT, rem = t % QT;
+            const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
+            const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
+            float qv[8];
+            float zt = 0.0f, mx = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ch = (e < 4 ? r0 : r1) + (e & 3);
+                const float sk = h2f_bits(kmeta[ch]);
+                const float zk = h2f_bits(kmeta[D + ch]);
+                qv[e] = qh[r][e] * sk;
+                zt = __builtin_fmaf(qh[r][e], __builtin_fmaf(MK, sk, zk), zt);
+                mx = fmaxf(mx, fabsf(qv[e]));
+            }
+            zt = grp_sum<QT>(zt);
+            mx = grp_max<QT>(mx);
+            const float sq = pow2_scale(mx);
+            if (n < G) {
+                _Float16 hv[8], lv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    split_hi_lo(qv[e] * sq, hv[2 * e], lv[2 * e]);
+                    split_hi_lo(qv[4 + e] * sq, hv[2 * e + 1], lv[2 * e + 1]);
+                }
+                const int off = ((gq * G + n) * NKB + 2 * pr) * 8;
+                *reinterpret_cast<uint4*>(bqimg + off) = __builtin_bit_cast(uint4, hv);
+                *reinterpret_cast<uint4*>(bqimg + 32 * G * NKB + off) = __builtin_bit_cast(uint4, lv);
+                if (rem == 0) { st_qz[n] = zt; st_iq[n] = 1.0f / sq; }
+            }
+        }
+        wave_sync();
+        if (mrow < G) {
+#pragma unroll
+            for (int k = 0; k < NKB; ++k) {
+                const int off = ((mgrp * G + mrow) * NKB + k) * 8;
+                bq_hi[k] = *reinterpret_cast<const h4_t*>(bqimg + off);
+                bq_lo[k] = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
+            }
+        }
+
+        // ---- scores: q.K^T on the matrix cores, per 16-token M-block ----
+#pragma unroll
+        for (int mb = 0; mb < TILE / 16; ++mb) {
+            f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < NKB; ++k) {
+                const h4_t av = code_operand<KB, KW>(kw[mb], k);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_hi[k], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_lo[k], c, 0, 0, 0);
+            }
+            if (mrow < G)
+                *reinterpret_cast<f4_t*>(sc + mrow * TILE + 16 * mb + 4 * mgrp) = c;
+        }
+        wave_sync();
+
+        // ---- online softmax, dense: task t = (query t/16, lane group, pair) ----
+#pragma unroll
+        for (int r = 0; r < STMAX; ++r) {
+            const int t = lane + 64 * r;
+            const int n = t / 16, rem = t % 16;
+            const int gv = rem / 4, pr = rem % 4;
+            const int r0 = run0_of<VB>(32 * gv, 2 * pr), r1 = r0 + Codes<VB>::N / 2;
+            const bool live = n < G;
+            const int nn = live ? n : 0;
+            const float iq = st_iq[nn], qz = st_qz[nn];
+            float s[8], svv[8], zvv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = (e < 4 ? r0 : r1) + (e & 3);
+                const float rk = h2f_bits(kmeta[2 * D + tok]);
+                svv[e] = h2f_bits(vmeta[tok]);
+                zvv[e] = h2f_bits(vmeta[TILE + tok]);
+                s[e] = a.sm_scale * rk * __builtin_fmaf(sc[nn * TILE + tok], iq, qz);
+            }
+            float mt = s[0], smax = 0.0f;
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) smax = fmaxf(smax, fabsf(svv[e]));
+            mt = grp_max<16>(mt);
+            smax = grp_max<16>(smax);
+            const float mnew = fmaxf(m_run[r], mt);
+            const float al = exp2f((m_run[r] - mnew) * kLog2e);
+            const float sp = pow2_scale(smax);
+            float p[8], lt = 0.0f, pz = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = exp2f((s[e] - mnew) * kLog2e);
+                lt += p[e];
+                pz = __builtin_fmaf(p[e], __builtin_fmaf(MV, svv[e], zvv[e]), pz);
+            }
+            lt = grp_sum<16>(lt);
+            pz = grp_sum<16>(pz);
+            m_run[r] = mnew;
+            l_run[r] = l_run[r] * al + lt;
+            if (live) {
+                _Float16 hv[8], lv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    split_hi_lo(p[e] * svv[e] * sp, hv[2 * e], lv[2 * e]);
+                    split_hi_lo(p[4 + e] * svv[4 + e] * sp, hv[2 * e + 1], lv[2 * e + 1]);
+                }
+                const int off = ((gv * G + n) * NVB + 2 * pr) * 8;
+                *reinterpret_cast<uint4*>(paimg + off) = __builtin_bit_cast(uint4, hv);
+                *reinterpret_cast<uint4*>(paimg + 256 * G + off) = __builtin_bit_cast(uint4, lv);
+                if (rem == 0) {
+                    st_al[n] = al;
+                    st_pz[n] = pz;
+                    if (n == 0) st_ip[0] = 1.0f / sp;
+                }
+            }
+        }
+        wave_sync();
+        if (mrow < G) {
+#pragma unroll
+            for (int k = 0; k < NVB; ++k) {
+                const int off = ((mgrp * G + mrow) * NVB + k) * 8;
+                pa_hi[k] = *reinterpret_cast<const h4_t*>(paimg + off);
+                pa_lo[k] = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
+            }
+        }
+
+        // ---- p.V on the matrix cores, per 16-channel N-block ----
+#pragma unroll
+        for (int nb = 0; nb < NKB; ++nb) {
+            f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < NVB; ++k) {
+                const h4_t bv = code_operand<VB, VW>(vw[nb], k);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_hi[k], bv, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_lo[k], bv, c, 0, 0, 0);
+            }
+            if (4 * mgrp < G)
+                *reinterpret_cast<f4_t*>(pvc + (16 * nb + mrow) * GP + 4 * mgrp) = c;
+        }
+        wave_sync();
+
+        // ---- dense update of the accumulator ----
+        {
+            const float ip = st_ip[0];
+#pragma unroll
+            for (int r = 0; r < CPL_E; ++r) {
+                const int ch = lane + 64 * r;
+                const float cv = h2f_bits(vmeta[2 * TILE + ch]);
+#pragma unroll
+                for (int n = 0; n < GMAX; ++n) {
+                    if (n < G) {
+                        const float upd = cv * __builtin_fmaf(pvc[ch * GP + n], ip, st_pz[n]);
+                        acc[r][n] = __builtin_fmaf(acc[r][n], st_al[n], upd);
+                    }
+                }
+            }
+        }
+        wave_sync();
+    }
+
+    // ---- partial result of this split: (m, l, acc[D]) per query head ----
+#pragma unroll
+    for (int r = 0; r < CPL_E; ++r) {
+        const int ch = lane + 64 * r;
+#pragma unroll
+        for (int n = 0; n < GMAX; ++n) {
+            if (n < G) {
+                const int h = g * G + n;
+                float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_splits + split) * (D + 2);
+                p[2 + ch] = acc[r][n];
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < STMAX; ++r) {
+        const int t = lane + 64 * r;
+        const int n = t / 16;
+        if (n < G && (t % 16) == 0) {
+            const int h = g * G + n;
+            float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_splits + split) * (D + 2);
+            p[0] = m_run[r];
+            p[1] = l_run[r];
+        }
+    }
+}
+
 template <int D>
 __device__ void lds_fwht(float* v, int rows) {
     const int tid = threadIdx.x;
@@ -56,158 +513,20 @@ __device__ void lds_fwht(float* v, int rows) {
         for (int k = tid; k < rows * D / 2; k += blockDim.x) {
             const int r = k / (D / 2), p = k % (D / 2);
             const int lo = (p / h) * 2 * h + (p % h), hi = lo + h;
-            const float a = v[r * D + lo], b = v[r * D + hi];
-            v[r * D + lo] = a + b;
-            v[r * D + hi] = a - b;
+            const float x = v[r * D + lo], y = v[r * D + hi];
+            v[r * D + lo] = x + y;
+            v[r * D + hi] = x - y;
         }
         __syncthreads();
     }
-    const float sc = 1.0f / __builtin_sqrtf((float)D);
-    for (int k = tid; k < rows * D; k += blockDim.x) v[k] *= sc;
+    const float s = 1.0f / __builtin_sqrtf((float)D);
+    for (int k = tid; k < rows * D; k += blockDim.x) v[k] *= s;
     __syncthreads();
-}
-
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(AttnArgs a) {
-    constexpr int KCB = TILE * D * KB / 8, VCB = TILE * D * VB / 8;
-    constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
-    constexpr uint32_t KMASK = (1u << KB) - 1, VMASK = (1u << VB) - 1;
-    constexpr float MK = 0.5f * (float)KMASK, MV = 0.5f * (float)VMASK;
-    constexpr int GMAX = 16;
-    __shared__ float qrot[GMAX * D];
-    __shared__ float qs[GMAX * D];
-    __shared__ float sc[GMAX * TILE];
-    __shared__ float qz[GMAX], pz[GMAX], alpha[GMAX], mrun[GMAX], lrun[GMAX];
-    __shared__ uint4 kimg[(KCB + 2 * KMH) / 16];
-    __shared__ uint4 vimg[(VCB + 2 * VMH) / 16];
-
-    const int tid = threadIdx.x;
-    const int G = a.n_q_heads / a.n_kv_heads;
-    const int blk = blockIdx.x;
-    const int split = blk % a.n_splits;
-    const int bg = blk / a.n_splits;
-    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    const int t0 = split * a.tiles_per_split;
-    int t1 = t0 + a.tiles_per_split;
-    if (t1 > a.tiles_per_seq) t1 = a.tiles_per_seq;
-
-    // rotated queries of the group
-    for (int k = tid; k < G * D; k += ATT_THREADS) {
-        const int hh = k / D, j = k % D;
-        const int h = g * G + hh;
-        qrot[k] = (j < a.d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + h) * a.d0 + j]) : 0.0f;
-    }
-    if (tid < G) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
-    __syncthreads();
-    lds_fwht<D>(qrot, G);
-
-    float acc[GMAX * D / ATT_THREADS > 0 ? GMAX * D / ATT_THREADS : 1];
-    const int npairs = G * D;
-#pragma unroll
-    for (int r = 0; r < (int)(sizeof(acc) / sizeof(float)); ++r) acc[r] = 0.0f;
-
-    const uint8_t* kcode = reinterpret_cast<const uint8_t*>(kimg);
-    const uint16_t* kmeta = reinterpret_cast<const uint16_t*>(kcode + KCB);
-    const uint8_t* vcode = reinterpret_cast<const uint8_t*>(vimg);
-    const uint16_t* vmeta = reinterpret_cast<const uint16_t*>(vcode + VCB);
-
-    for (int ti = t0; ti < t1; ++ti) {
-        const int64_t tile = (int64_t)bg * a.tiles_per_seq + ti;
-        {
-            const uint4* src = reinterpret_cast<const uint4*>(a.kc + tile * KCB);
-            for (int k = tid; k < KCB / 16; k += ATT_THREADS) kimg[k] = src[k];
-            const uint4* msrc = reinterpret_cast<const uint4*>(a.km + tile * KMH);
-            for (int k = tid; k < 2 * KMH / 16; k += ATT_THREADS) kimg[KCB / 16 + k] = msrc[k];
-            const uint4* vsrc = reinterpret_cast<const uint4*>(a.vc + tile * VCB);
-            for (int k = tid; k < VCB / 16; k += ATT_THREADS) vimg[k] = vsrc[k];
-            const uint4* vmsrc = reinterpret_cast<const uint4*>(a.vm + tile * VMH);
-            for (int k = tid; k < 2 * VMH / 16; k += ATT_THREADS) vimg[VCB / 16 + k] = vmsrc[k];
-        }
-        __syncthreads();
-        // q folded with the per-channel K scale; zero-point term per head
-        for (int k = tid; k < G * D; k += ATT_THREADS) qs[k] = qrot[k] * h2f_bits(kmeta[k % D]);
-        if (tid < G) {
-            float z = 0.0f;
-            for (int j = 0; j < D; ++j)
-                z = __builtin_fmaf(qrot[tid * D + j],
-                                   __builtin_fmaf(MK, h2f_bits(kmeta[j]), h2f_bits(kmeta[D + j])), z);
-            qz[tid] = z;
-        }
-        __syncthreads();
-        // scores
-        for (int k = tid; k < G * TILE; k += ATT_THREADS) {
-            const int hh = k / TILE, t = k % TILE;
-            float s = 0.0f;
-            for (int j = 0; j < D; ++j) {
-                const int64_t e = (int64_t)t * D + j;
-                const uint32_t c = (kcode[(e * KB) >> 3] >> ((e * KB) & 7)) & KMASK;
-                s = __builtin_fmaf(qs[hh * D + j], (float)c - MK, s);
-            }
-            sc[k] = a.sm_scale * h2f_bits(kmeta[2 * D + t]) * (s + qz[hh]);
-        }
-        __syncthreads();
-        // online softmax, one wave per head
-        {
-            const int w = tid / 64, lane = tid % 64;
-            for (int hh = w; hh < G; hh += ATT_THREADS / 64) {
-                float m = fmaxf(sc[hh * TILE + lane], sc[hh * TILE + 64 + lane]);
-                for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-                const float mnew = fmaxf(mrun[hh], m);
-                const float p0 = __expf(sc[hh * TILE + lane] - mnew);
-                const float p1 = __expf(sc[hh * TILE + 64 + lane] - mnew);
-                float l = p0 + p1;
-                const float sv0 = h2f_bits(vmeta[lane]), sv1 = h2f_bits(vmeta[64 + lane]);
-                const float zv0 = h2f_bits(vmeta[TILE + lane]), zv1 = h2f_bits(vmeta[TILE + 64 + lane]);
-                float z = p0 * __builtin_fmaf(MV, sv0, zv0) + p1 * __builtin_fmaf(MV, sv1, zv1);
-                for (int o = 32; o > 0; o >>= 1) { l += __shfl_xor(l, o); z += __shfl_xor(z, o); }
-                sc[hh * TILE + lane] = p0 * sv0;
-                sc[hh * TILE + 64 + lane] = p1 * sv1;
-                if (lane == 0) {
-                    const float al = __expf(mrun[hh] - mnew);
-                    alpha[hh] = al;
-                    lrun[hh] = lrun[hh] * al + l;
-                    mrun[hh] = mnew;
-                    pz[hh] = z;
-                }
-            }
-        }
-        __syncthreads();
-        // p V accumulation (per channel, over the tile's tokens)
-#pragma unroll
-        for (int r = 0; r < (int)(sizeof(acc) / sizeof(float)); ++r) {
-            const int k = tid + r * ATT_THREADS;
-            if (k < npairs) {
-                const int hh = k / D, j = k % D;
-                float s = 0.0f;
-                for (int t = 0; t < TILE; ++t) {
-                    const int64_t e = (int64_t)j * TILE + t;
-                    const uint32_t c = (vcode[(e * VB) >> 3] >> ((e * VB) & 7)) & VMASK;
-                    s = __builtin_fmaf(sc[hh * TILE + t], (float)c - MV, s);
-                }
-                acc[r] = acc[r] * alpha[hh] + h2f_bits(vmeta[2 * TILE + j]) * (s + pz[hh]);
-            }
-        }
-        __syncthreads();
-    }
-
-    // partial out: [b][h][split][D + 2] = (m, l, acc)
-#pragma unroll
-    for (int r = 0; r < (int)(sizeof(acc) / sizeof(float)); ++r) {
-        const int k = tid + r * ATT_THREADS;
-        if (k < npairs) {
-            const int hh = k / D, j = k % D;
-            const int h = g * G + hh;
-            float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_splits + split) * (D + 2);
-            p[2 + j] = acc[r];
-            if (j == 0) { p[0] = mrun[hh]; p[1] = lrun[hh]; }
-        }
-    }
 }
 
 template <int D>
-__global__ __launch_bounds__(ATT_THREADS) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     __shared__ float o[D];
-    __shared__ float wsum[1];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;   // b * n_q_heads + h
     const float* p = a.ws + (size_t)bh * a.n_splits * (D + 2);
@@ -216,20 +535,19 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_combine_kernel(AttnArgs a) {
     float L = 0.0f;
     for (int s = 0; s < a.n_splits; ++s) {
         const float ms = p[s * (D + 2)];
-        if (ms != -INFINITY) L += p[s * (D + 2) + 1] * __expf(ms - M);
+        if (ms != -INFINITY) L += p[s * (D + 2) + 1] * exp2f((ms - M) * kLog2e);
     }
-    if (tid == 0) wsum[0] = L;
-    for (int j = tid; j < D; j += ATT_THREADS) {
+    for (int j = tid; j < D; j += blockDim.x) {
         float v = 0.0f;
         for (int s = 0; s < a.n_splits; ++s) {
             const float ms = p[s * (D + 2)];
-            if (ms != -INFINITY) v += p[s * (D + 2) + 2 + j] * __expf(ms - M);
+            if (ms != -INFINITY) v += p[s * (D + 2) + 2 + j] * exp2f((ms - M) * kLog2e);
         }
         o[j] = (L > 0.0f) ? v / L : 0.0f;
     }
     __syncthreads();
     lds_fwht<D>(o, 1);
-    for (int j = tid; j < a.d0; j += ATT_THREADS) a.out[(size_t)bh * a.d0 + j] = o[j];
+    for (int j = tid; j < a.d0; j += blockDim.x) a.out[(size_t)bh * a.d0 + j] = o[j];
 }
 
 __global__ void fill_zero_kernel(float* out, int64_t n) {
@@ -237,24 +555,37 @@ __global__ void fill_zero_kernel(float* out, int64_t n) {
     if (i < n) out[i] = 0.0f;
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int GMAX>
 static hipError_t launch_att(const AttnArgs& a, hipStream_t s) {
-    const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * a.n_splits;
-    hipLaunchKernelGGL((attn_partial_kernel<D, KB, VB>), dim3((unsigned)blocks), dim3(ATT_THREADS),
-                       0, s, a);
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const int per_wave = AttnLds<D>::bytes(G);
+    int wpb = 65536 / per_wave;
+    if (wpb > 4) wpb = 4;
+    if (wpb < 1) wpb = 1;
+    const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
+    const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
+    hipLaunchKernelGGL((attn_partial_kernel<D, KB, VB, GMAX>), dim3((unsigned)blocks),
+                       dim3(64 * wpb), (size_t)per_wave * wpb, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(a.batch * a.n_q_heads)),
-                       dim3(ATT_THREADS), 0, s, a);
+                       dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+static hipError_t launch_att_g(const AttnArgs& a, hipStream_t s) {
+    const int G = a.n_q_heads / a.n_kv_heads;
+    if (G <= 4) return launch_att<D, KB, VB, 4>(a, s);
+    return launch_att<D, KB, VB, 16>(a, s);
 }
 
 template <int D>
 static hipError_t launch_att_bits(const AttnArgs& a, int kb, int vb, hipStream_t s) {
-    if (kb == 4 && vb == 2) return launch_att<D, 4, 2>(a, s);
-    if (kb == 4 && vb == 4) return launch_att<D, 4, 4>(a, s);
-    if (kb == 2 && vb == 2) return launch_att<D, 2, 2>(a, s);
-    return launch_att<D, 2, 4>(a, s);
+    if (kb == 4 && vb == 2) return launch_att_g<D, 4, 2>(a, s);
+    if (kb == 4 && vb == 4) return launch_att_g<D, 4, 4>(a, s);
+    if (kb == 2 && vb == 2) return launch_att_g<D, 2, 2>(a, s);
+    return launch_att_g<D, 2, 4>(a, s);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_t s) {
