@@ -116,12 +116,6 @@ __device__ __forceinline__ int run0_of(int group_base, int kbase) {
     return group_base + N * (kbase / Q) + 2 * (kbase % Q);
 }
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // reductions over aligned groups of W lanes (W = 8, 16, 32)
 template <int W>
 __device__ __forceinline__ float grp_sum(float v) {

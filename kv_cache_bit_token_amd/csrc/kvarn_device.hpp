@@ -109,14 +109,62 @@ __device__ __forceinline__ void xstage(float (&x)[TPL][CPL], float sg) {
         for (int c = 0; c < CPL; ++c) x[i][c] = __builtin_fmaf(dpp<CTRL>(x[i][c]), sg, x[i][c]);
 }
 
+// One cross-lane stage as single instructions: v_fmac_f32 with a DPP source
+// computes x += sign * x(partner lane) in place.  The compiler does not form
+// this DPP multiply-add from the builtins, so it is written out; the leading
+// s_nop 1 gives the two wait states a DPP read needs after a VALU write of
+// the same VGPR (inside a block every instruction reads a different VGPR,
+// written by the previous stage).
+#define KVARN_FMAC_DPP_BLOCK(CTRL)                                                              \
+    asm volatile("s_nop 1\n"                                                                   \
+                 "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"            \
+                 "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"          \
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),     \
+                   "+v"(r[6]), "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]),   \
+                   "+v"(r[12]), "+v"(r[13]), "+v"(r[14]), "+v"(r[15])                           \
+                 : "v"(sg))
+
+template <int CTRL>
+__device__ __forceinline__ void xstage_fmac(float (&r)[CPL], float sg) {
+    if constexpr (CTRL == DPP_XOR1) KVARN_FMAC_DPP_BLOCK("quad_perm:[1,0,3,2]");
+    else if constexpr (CTRL == DPP_XOR2) KVARN_FMAC_DPP_BLOCK("quad_perm:[2,3,0,1]");
+    else if constexpr (CTRL == DPP_HMIR) KVARN_FMAC_DPP_BLOCK("row_half_mirror");
+    else KVARN_FMAC_DPP_BLOCK("row_ror:8");
+}
+
 // Cross-lane stages; cb = lane position in its row-group.
 template <int R>
 __device__ __forceinline__ void fwht_crosslane(float (&x)[TPL][CPL], int cb) {
     using N = Net<R>;
-    xstage<DPP_XOR1>(x, sign_of(N::up0(cb)));
-    xstage<DPP_XOR2>(x, sign_of(N::up1(cb)));
-    if constexpr (R >= 8) xstage<DPP_HMIR>(x, sign_of(N::up2(cb)));
-    if constexpr (R >= 16) xstage<DPP_ROR8>(x, sign_of(N::up3(cb)));
+    const float s0 = sign_of(N::up0(cb)), s1 = sign_of(N::up1(cb));
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) xstage_fmac<DPP_XOR1>(x[i], s0);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) xstage_fmac<DPP_XOR2>(x[i], s1);
+    if constexpr (R >= 8) {
+        const float s2 = sign_of(N::up2(cb));
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) xstage_fmac<DPP_HMIR>(x[i], s2);
+    }
+    if constexpr (R >= 16) {
+        const float s3 = sign_of(N::up3(cb));
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) xstage_fmac<DPP_ROR8>(x[i], s3);
+    }
 }
 
 // All-reduce across the R lanes of a row-group (every lane gets the result;
@@ -157,6 +205,14 @@ __device__ __forceinline__ uint16_t f2h_bits(float v) {
 }
 __device__ __forceinline__ float h2f_bits(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Orders the LDS accesses of one wavefront: what its lanes wrote before is
+// visible to its lanes after (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int D> constexpr int padded_ok() { return D == 64 || D == 128 || D == 256; }

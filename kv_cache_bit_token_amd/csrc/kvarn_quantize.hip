@@ -11,8 +11,8 @@
 //
 // One workgroup = one tile (K or V), 2*D threads, the tile held in VGPRs as
 // fp32 (see kvarn_device.hpp for the lane layout and the transform).  The
-// input is read from HBM exactly once; codes and meta are staged in LDS and
-// written out with 16-byte stores.
+// input is read from HBM exactly once; codes and meta are written straight
+// from registers.
 //
 // Arithmetic, equal to the stated method in exact arithmetic:
 //  * The transform runs unscaled: X' = sqrt(D) * Xt.  The normalised tile is
@@ -23,16 +23,30 @@
 //    these products directly (C[c] = exp(l_c), R[t] = exp(l_r)) and
 //    recomputes each std from X' and the current cross-axis factors, the
 //    same quantity without an exp/log round trip.
+//  * Each std comes from the raw moments sum(v) and sum(v^2) of v = X' * f
+//    (f the cross-axis factor) in one pass; the factor's reciprocal is the
+//    hardware reciprocal square root of the variance (about 1 ulp).  Where
+//    the mean is large next to the spread (mean^2 > var/4, or var <= 0,
+//    which also catches flat groups) the moments lose accuracy to
+//    cancellation, and that pass is recomputed with the two-pass centred
+//    formula: per tile for a column pass, per token for a row pass.
 //  * A K group (one channel) is scaled by its own column factor, which
 //    cancels in its codes and folds back in SK, ZK: the kernel quantises
 //    X' * (1/R[t]) directly.  Likewise V quantises X' * (1/C[c]) and the row
 //    factor cancels, so V skips the last row pass (its result is not used).
-//  * Standard deviations are two-pass (mean first, then centred sum of
-//    squares), population (divide by the group size).
+//  * A code is u = (v - z) / s rounded to the nearest integer, ties to even,
+//    by the unsigned-byte conversion (which also clamps to [0, 255]), packed
+//    four to a register and merged with shifts.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 
 namespace kvarn {
+
+// round-to-nearest-even of u into byte SEL of acc (clamped to 0..255)
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_u8(float u, uint32_t acc) {
+    return __builtin_amdgcn_cvt_pk_u8_f32(u, SEL, acc);
+}
 
 template <int D, int BITS, bool IS_K>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, int d0, int n_iters,
@@ -41,8 +55,6 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     constexpr int R = D / CPL;          // lanes per row-group
     constexpr int NT = 2 * D;           // threads
     constexpr int L = (1 << BITS) - 1;  // top code
-    constexpr int CODE_BYTES = TILE * D * BITS / 8;
-    constexpr int META_HALVES = IS_K ? 2 * D + TILE : 2 * TILE + D;
     using N = Net<R>;
 
     const int tid = threadIdx.x;
@@ -53,9 +65,19 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     const float sqrtD = __builtin_sqrtf((float)D);
     const float rsqrtD = 1.0f / sqrtD;
 
-    float* part = lds;                    // [32][D] column partials
-    float* colv = lds + 32 * D;           // [D] broadcast of column stats
-    float* colv2 = colv + D;              // [D]
+    // Column partials (float2 per channel slot): thread n keeps its 16 at
+    // entries [PST n, PST n + 16).  The odd stride puts the 32 lanes of a
+    // half-wave on distinct bank pairs when they store the same slot.  The
+    // reducer of lane position rp, half rh, sums the token groups
+    // tb = k % DL + rh DL + (k / DL) 2 DL (k < 16, DL = 16 / R), so that the
+    // two halves of a half-wave read entries 16 apart: no collision either.
+    constexpr int PST = CPL + 1;
+    constexpr int DL = 16 / R;
+    float2* part = reinterpret_cast<float2*>(lds);   // [2D][PST]
+    float* colv = lds + 4 * PST * D;                 // [D] broadcast of column stats
+    float* colv2 = colv + D;                         // [D]
+    int* flag = reinterpret_cast<int*>(colv2 + D);   // [1] column-pass fallback request
+    float* gsum = colv2 + D + 4;                     // [16] gauge partials
 
     // ---------------- load (one HBM read) + pad ----------------
     float x[TPL][CPL];
@@ -85,62 +107,90 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     fwht_crosslane<R>(x, cb);
 
     // ---------------- normalisation ----------------
-    float a[TPL];      // 1 / R[t] for my tokens
-    float Rt[TPL];     // R[t] = exp(l_r[t])
+    float a[TPL], Rt[TPL];          // 1 / R[t] and R[t] = exp(l_r[t]) for my tokens
 #pragma unroll
     for (int i = 0; i < TPL; ++i) { a[i] = 1.0f; Rt[i] = 1.0f; }
-    float b[CPL];      // 1 / C[c] for my channels (unscaled units)
+    float b[CPL];                   // 1 / C[c] for my channels (unscaled units)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) b[c] = rsqrtD;
 
-    // reducer role: position p = tid >> 1 (lane-position space), half hh
+    // reducer role: position p = tid >> 1 (lane-position space), half rh
     const int rp = tid >> 1, rh = tid & 1;
+    const float2* rpart = part + PST * (16 * rh + (rp >> 4)) + (rp & 15);
+    float2* wpart = part + PST * tid;
     float Cp = sqrtD;   // column factor of position rp, unscaled units (exp(l_c) * sqrt(D))
+    float Cinv = rsqrtD;
+    if (tid == 0) *flag = 0;
 
     for (int it = 0; it < n_iters; ++it) {
-        // ---- column pass: mean over tokens of x * a ----
+        // ---- column pass: raw moments over tokens of x * a ----
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            float s = 0.0f;
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) s = __builtin_fmaf(x[i][c], a[i], s);
-            part[tb * D + 16 * cb + c] = s;
-        }
-        __syncthreads();
-        float cmean;
-        {
-            float s = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) s += part[(rh * 16 + k) * D + rp];
-            s += dpp<DPP_XOR1>(s);
-            cmean = s * (1.0f / TILE);
-            if (rh == 0) colv[rp] = cmean;
-        }
-        __syncthreads();
-        float m[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) m[c] = colv[16 * cb + c];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            float q = 0.0f;
+            float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                float d = __builtin_fmaf(x[i][c], a[i], -m[c]);
-                q = __builtin_fmaf(d, d, q);
+                const float v = x[i][c] * a[i];
+                s1 += v;
+                s2 = __builtin_fmaf(v, v, s2);
             }
-            part[tb * D + 16 * cb + c] = q;
+            wpart[c] = make_float2(s1, s2);
         }
         __syncthreads();
+        const float Cprev = Cp;
+        float cmean;
         {
-            float q = 0.0f;
+            float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) q += part[(rh * 16 + k) * D + rp];
-            q += dpp<DPP_XOR1>(q);
-            const float sd = __builtin_sqrtf(q * (1.0f / TILE));
-            if (!is_flat(sd, cmean)) Cp = sd;
-            if (rh == 0) colv[rp] = 1.0f / Cp;
+            for (int k = 0; k < 16; ++k) {
+                const float2 v = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
+                s1 += v.x;
+                s2 += v.y;
+            }
+            s1 += dpp<DPP_XOR1>(s1);
+            s2 += dpp<DPP_XOR1>(s2);
+            cmean = s1 * (1.0f / TILE);
+            const float var = __builtin_fmaf(-cmean, cmean, s2 * (1.0f / TILE));
+            if ((var > 0.0f) && (cmean * cmean <= 0.25f * var)) {
+                Cinv = __builtin_amdgcn_rsqf(var);
+                Cp = var * Cinv;
+            } else {
+                *flag = 1;
+            }
+            if (rh == 0) colv[rp] = Cinv;
         }
         __syncthreads();
+        if (*flag) {
+            // fallback: centred two-pass stds for every column of this pass
+            // (the means are those of the raw pass)
+            if (rh == 0) colv2[rp] = cmean;
+            __syncthreads();   // every thread has read the flag
+            if (tid == 0) *flag = 0;
+            float m[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) m[c] = colv2[16 * cb + c];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float q = 0.0f;
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const float d = __builtin_fmaf(x[i][c], a[i], -m[c]);
+                    q = __builtin_fmaf(d, d, q);
+                }
+                wpart[c].x = q;
+            }
+            __syncthreads();
+            {
+                float q = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) q += rpart[PST * R * (k % DL + (k / DL) * 2 * DL)].x;
+                q += dpp<DPP_XOR1>(q);
+                const float sd = __builtin_sqrtf(q * (1.0f / TILE));
+                Cp = is_flat(sd, cmean) ? Cprev : sd;
+                Cinv = 1.0f / Cp;
+                if (rh == 0) colv[rp] = Cinv;
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int c = 0; c < CPL; ++c) b[c] = colv[16 * cb + c];
 
@@ -148,19 +198,32 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         if (!IS_K && it == n_iters - 1) break;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            float s = 0.0f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) s = __builtin_fmaf(x[i][c], b[c], s);
-            const float rmean = rg_sum<R>(s) * (1.0f / D);
-            float q = 0.0f;
+            float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                float d = __builtin_fmaf(x[i][c], b[c], -rmean);
-                q = __builtin_fmaf(d, d, q);
+                const float v = x[i][c] * b[c];
+                s1 += v;
+                s2 = __builtin_fmaf(v, v, s2);
             }
-            const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
-            if (!is_flat(sd, rmean)) Rt[i] = sd;
-            a[i] = 1.0f / Rt[i];
+            s1 = rg_sum<R>(s1);
+            s2 = rg_sum<R>(s2);
+            const float mean = s1 * (1.0f / D);
+            const float var = __builtin_fmaf(-mean, mean, s2 * (1.0f / D));
+            if ((var > 0.0f) && (mean * mean <= 0.25f * var)) {
+                a[i] = __builtin_amdgcn_rsqf(var);
+                Rt[i] = var * a[i];
+            } else {
+                // fallback for this token (uniform across its row-group)
+                float q = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float d = __builtin_fmaf(x[i][c], b[c], -mean);
+                    q = __builtin_fmaf(d, d, q);
+                }
+                const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
+                if (!is_flat(sd, mean)) Rt[i] = sd;
+                a[i] = 1.0f / Rt[i];
+            }
         }
     }
 
@@ -170,7 +233,6 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     // column factors) so the stored fp16 factors stay in range even when the
     // iteration drifts the two sets apart.  Codes are unaffected; only the
     // stored SK/ZK/RK (K) and SV/ZV/CV (V) see G.
-    float* gsum = lds + 66 * D;
     float G, invG;
     {
         float s = logf(Cp * rsqrtD);   // both lanes of a position: the sum is 2x
@@ -185,167 +247,196 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         G = expf(mean_lc);
         invG = expf(-mean_lc);
     }
+    // Sylvester channel index of the reducer's lane position
+    const int kpos = 16 * N::nu(rp >> 4) + (rp & 15);
 
-    // ---------------- quantisation parameters ----------------
-    uint8_t* cimg = reinterpret_cast<uint8_t*>(lds);                  // packed code image
-    uint16_t* mimg = reinterpret_cast<uint16_t*>(lds + CODE_BYTES / 4);  // meta image
-    uint32_t code[TPL][CPL];
-
+    // ---------------- quantisation, packing, stores ----------------
     if constexpr (IS_K) {
         // K: one group per channel, over the 128 tokens: values v = x * a[t]
-        float v[TPL][CPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) v[i][c] = x[i][c] * a[i];
-        __syncthreads();   // LDS part[] reuse
+            for (int c = 0; c < CPL; ++c) x[i][c] *= a[i];
+        // (min, max) partials, same layout as the column moments
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            float mn = v[0][c], mx = v[0][c];
-#pragma unroll
-            for (int i = 1; i < TPL; ++i) { mn = fminf(mn, v[i][c]); mx = fmaxf(mx, v[i][c]); }
-            part[tb * D + 16 * cb + c] = mn;
-            part[32 * D + 2 * D + tb * D + 16 * cb + c] = mx;   // second buffer after colv/colv2
+            float mn = fminf(fminf(x[0][c], x[1][c]), fminf(x[2][c], x[3][c]));
+            float mx = fmaxf(fmaxf(x[0][c], x[1][c]), fmaxf(x[2][c], x[3][c]));
+            wpart[c] = make_float2(mn, mx);
         }
         __syncthreads();
-        float zk, sk;
         {
-            float mn = part[(rh * 16) * D + rp], mx = part[32 * D + 2 * D + (rh * 16) * D + rp];
+            float mn = rpart[0].x, mx = rpart[0].y;
 #pragma unroll
             for (int k = 1; k < 16; ++k) {
-                mn = fminf(mn, part[(rh * 16 + k) * D + rp]);
-                mx = fmaxf(mx, part[32 * D + 2 * D + (rh * 16 + k) * D + rp]);
+                const float2 v = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
+                mn = fminf(mn, v.x);
+                mx = fmaxf(mx, v.y);
             }
             mn = fminf(mn, dpp<DPP_XOR1>(mn));
             mx = fmaxf(mx, dpp<DPP_XOR1>(mx));
-            zk = mn;
-            sk = (mx - mn) / (float)L;
+            const float zk = mn;
+            const float sk = (mx - mn) / (float)L;
             const float inv = (mx > mn) ? 1.0f / sk : 0.0f;
-            if (rh == 0) { colv[rp] = inv; colv2[rp] = -zk * inv; }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float inv = colv[16 * cb + c], off = colv2[16 * cb + c];
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                float u = __builtin_fmaf(v[i][c], inv, off);
-                float r = __builtin_rintf(u);
-                r = fminf(fmaxf(r, 0.0f), (float)L);
-                code[i][c] = (uint32_t)r;
+            if (rh == 0) {
+                colv[rp] = inv;
+                colv2[rp] = -zk * inv;
+                meta_out[kpos] = f2h_bits(sk * rsqrtD * invG);        // SK
+                meta_out[D + kpos] = f2h_bits(zk * rsqrtD * invG);    // ZK
             }
         }
-        __syncthreads();   // image overwrites part[]
-        // meta: SK, ZK by the reducers (rotated channel index), RK by lane cb == 0
-        if (rh == 0) {
-            const int k = 16 * N::nu(rp >> 4) + (rp & 15);
-            mimg[k] = f2h_bits(sk * rsqrtD * invG);
-            mimg[D + k] = f2h_bits(zk * rsqrtD * invG);
+        __syncthreads();
+        if (cb == 0) {   // RK of my 4 tokens
+            const uint32_t lo = f2h_bits(Rt[0] * G) | ((uint32_t)f2h_bits(Rt[1] * G) << 16);
+            const uint32_t hi = f2h_bits(Rt[2] * G) | ((uint32_t)f2h_bits(Rt[3] * G) << 16);
+            *reinterpret_cast<uint2*>(meta_out + 2 * D + 4 * tb) = make_uint2(lo, hi);
         }
-        if (cb == 0) {
+        float inv[CPL], off[CPL];
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) mimg[2 * D + 4 * tb + i] = f2h_bits(Rt[i] * G);
+        for (int c = 0; c < CPL; ++c) { inv[c] = colv[16 * cb + c]; off[c] = colv2[16 * cb + c]; }
+        // token-major stream: token t, channels 16*ob .. +15 are contiguous
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            float u[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) u[c] = __builtin_fmaf(x[i][c], inv[c], off[c]);
+            const int t = 4 * tb + i;
+            if constexpr (BITS == 4) {
+                uint32_t w[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float* q = u + 8 * h;
+                    const uint32_t ev = cvt_u8<3>(q[6], cvt_u8<2>(q[4], cvt_u8<1>(q[2], cvt_u8<0>(q[0], 0u))));
+                    const uint32_t od = cvt_u8<3>(q[7], cvt_u8<2>(q[5], cvt_u8<1>(q[3], cvt_u8<0>(q[1], 0u))));
+                    w[h] = ev | (od << 4);
+                }
+                *reinterpret_cast<uint2*>(codes_out + (t * D + 16 * ob) / 2) = make_uint2(w[0], w[1]);
+            } else {
+                uint32_t p[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    p[m] = cvt_u8<3>(u[12 + m], cvt_u8<2>(u[8 + m], cvt_u8<1>(u[4 + m], cvt_u8<0>(u[m], 0u))));
+                *reinterpret_cast<uint32_t*>(codes_out + (t * D + 16 * ob) / 4) =
+                    p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6);
+            }
         }
     } else {
         // V: one group per token, over the D channels: values v = x * b[c]
-        float v[TPL][CPL];
-        float inv[TPL], off[TPL], zv[TPL], sv[TPL];
+        float inv[TPL], off[TPL];
+        uint32_t sv2[TPL / 2], zv2[TPL / 2];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            float mn = 3.0e38f, mx = -3.0e38f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                v[i][c] = x[i][c] * b[c];
-                mn = fminf(mn, v[i][c]);
-                mx = fmaxf(mx, v[i][c]);
-            }
+            for (int c = 0; c < CPL; ++c) x[i][c] *= b[c];
+            float mn = x[i][0], mx = x[i][0];
+#pragma unroll
+            for (int c = 1; c < CPL; ++c) { mn = fminf(mn, x[i][c]); mx = fmaxf(mx, x[i][c]); }
             mn = rg_min<R>(mn);
             mx = rg_max<R>(mx);
-            zv[i] = mn;
-            sv[i] = (mx - mn) / (float)L;
-            inv[i] = (mx > mn) ? 1.0f / sv[i] : 0.0f;
+            const float sv = (mx - mn) / (float)L;
+            inv[i] = (mx > mn) ? 1.0f / sv : 0.0f;
             off[i] = -mn * inv[i];
+            const uint32_t hs = f2h_bits(sv * G), hz = f2h_bits(mn * G);
+            if (i & 1) { sv2[i / 2] |= hs << 16; zv2[i / 2] |= hz << 16; }
+            else       { sv2[i / 2] = hs;        zv2[i / 2] = hz; }
         }
-#pragma unroll
-        for (int i = 0; i < TPL; ++i)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                float u = __builtin_fmaf(v[i][c], inv[i], off[i]);
-                float r = __builtin_rintf(u);
-                r = fminf(fmaxf(r, 0.0f), (float)L);
-                code[i][c] = (uint32_t)r;
-            }
-        __syncthreads();   // image overwrites part[]
-        if (cb == 0) {
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                mimg[4 * tb + i] = f2h_bits(sv[i] * G);
-                mimg[TILE + 4 * tb + i] = f2h_bits(zv[i] * G);
-            }
+        if (cb == 0) {   // SV, ZV of my 4 tokens
+            *reinterpret_cast<uint2*>(meta_out + 4 * tb) = make_uint2(sv2[0], sv2[1]);
+            *reinterpret_cast<uint2*>(meta_out + TILE + 4 * tb) = make_uint2(zv2[0], zv2[1]);
         }
-        if (rh == 0) {
-            const int k = 16 * N::nu(rp >> 4) + (rp & 15);
-            mimg[2 * TILE + k] = f2h_bits(Cp * rsqrtD * invG);
-        }
-    }
+        if (rh == 0) meta_out[2 * TILE + kpos] = f2h_bits(Cp * rsqrtD * invG);   // CV
 
-    // ---------------- pack into the LDS image ----------------
-    if constexpr (IS_K) {
-        // token-major: token t, channels 16*ob .. +15 are contiguous
+        // Channel-major stream: channel k's codes of tokens 4*tb .. +3 form
+        // BITS/2 bytes at k * (TILE * BITS / 8) + (BITS / 2) * tb.  Each lane packs
+        // its channels, then lanes that hold neighbouring token groups of the
+        // same channels swap through LDS (a transpose inside one wavefront)
+        // so that every lane stores whole 32-bit words.  The partials are no
+        // longer read by any wave (last read before the gauge barrier).
+        constexpr int ROWB = TILE * BITS / 8;   // bytes per channel row
+        uint32_t* xch = reinterpret_cast<uint32_t*>(lds);
+        if constexpr (BITS == 2) {
+            // p[q]: byte n = channel 16*ob + 4q + n, tokens 4*tb .. +3
+            uint32_t p[4];
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int t = 4 * tb + i;
-            if constexpr (BITS == 4) {
-                uint32_t w0 = 0, w1 = 0;
+            for (int q = 0; q < 4; ++q) {
+                uint32_t t4[TPL];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) { w0 |= code[i][c] << (4 * c); w1 |= code[i][8 + c] << (4 * c); }
-                *reinterpret_cast<uint2*>(cimg + (t * D + 16 * ob) / 2) = make_uint2(w0, w1);
-            } else {
-                uint32_t w = 0;
+                for (int i = 0; i < TPL; ++i) {
+                    const float* xr = x[i] + 4 * q;
+                    t4[i] = cvt_u8<3>(__builtin_fmaf(xr[3], inv[i], off[i]),
+                            cvt_u8<2>(__builtin_fmaf(xr[2], inv[i], off[i]),
+                            cvt_u8<1>(__builtin_fmaf(xr[1], inv[i], off[i]),
+                            cvt_u8<0>(__builtin_fmaf(xr[0], inv[i], off[i]), 0u))));
+                }
+                p[q] = t4[0] | (t4[1] << 2) | (t4[2] << 4) | (t4[3] << 6);
+            }
+            // group of 4 lanes: token groups tb = 4m + j, same channel block
+            *reinterpret_cast<uint4*>(xch + 4 * tid) = make_uint4(p[0], p[1], p[2], p[3]);
+            wave_sync();
+            const int j = tb & 3;
+            const int base = tid - j * R;   // lane of token group 4m
+            uint32_t r[4];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) w |= code[i][c] << (2 * c);
-                *reinterpret_cast<uint32_t*>(cimg + (t * D + 16 * ob) / 4) = w;
+            for (int jj = 0; jj < 4; ++jj) r[jj] = xch[4 * (base + jj * R) + j];
+            // 4x4 byte transpose: g[n] byte jj = r[jj] byte n
+            const uint32_t A = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+            const uint32_t B = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+            const uint32_t C = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+            const uint32_t E = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+            const uint32_t g[4] = {__builtin_amdgcn_perm(C, A, 0x05040100u),
+                                   __builtin_amdgcn_perm(C, A, 0x07060302u),
+                                   __builtin_amdgcn_perm(E, B, 0x05040100u),
+                                   __builtin_amdgcn_perm(E, B, 0x07060302u)};
+            const int m = tb >> 2;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int k = 16 * ob + 4 * j + n;
+                *reinterpret_cast<uint32_t*>(codes_out + k * ROWB + 4 * m) = g[n];
+            }
+        } else {
+            // p[q]: channel 16*ob + 2q + e -> bytes 2e (tokens 0,1), 2e + 1 (tokens 2,3)
+            uint32_t p[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int c0 = 2 * q, c1 = 2 * q + 1;
+                const uint32_t ev = cvt_u8<3>(__builtin_fmaf(x[2][c1], inv[2], off[2]),
+                                    cvt_u8<2>(__builtin_fmaf(x[0][c1], inv[0], off[0]),
+                                    cvt_u8<1>(__builtin_fmaf(x[2][c0], inv[2], off[2]),
+                                    cvt_u8<0>(__builtin_fmaf(x[0][c0], inv[0], off[0]), 0u))));
+                const uint32_t od = cvt_u8<3>(__builtin_fmaf(x[3][c1], inv[3], off[3]),
+                                    cvt_u8<2>(__builtin_fmaf(x[1][c1], inv[1], off[1]),
+                                    cvt_u8<1>(__builtin_fmaf(x[3][c0], inv[3], off[3]),
+                                    cvt_u8<0>(__builtin_fmaf(x[1][c0], inv[1], off[1]), 0u))));
+                p[q] = ev | (od << 4);
+            }
+            // pairs of lanes: token groups tb = 2m + j
+            *reinterpret_cast<uint4*>(xch + 8 * tid) = make_uint4(p[0], p[1], p[2], p[3]);
+            *reinterpret_cast<uint4*>(xch + 8 * tid + 4) = make_uint4(p[4], p[5], p[6], p[7]);
+            wave_sync();
+            const int j = tb & 1;
+            const int base = tid - j * R;
+            const int m = tb >> 1;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t r0 = xch[8 * base + q], r1 = xch[8 * (base + R) + q];
+                // channel 2q + j: halfword j of each lane's word
+                const uint32_t g = j ? __builtin_amdgcn_perm(r1, r0, 0x07060302u)
+                                     : __builtin_amdgcn_perm(r1, r0, 0x05040100u);
+                const int k = 16 * ob + 2 * q + j;
+                *reinterpret_cast<uint32_t*>(codes_out + k * ROWB + 4 * m) = g;
             }
         }
-    } else {
-        // channel-major: channel k, tokens 4*tb .. +3 are contiguous
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int k = 16 * ob + c;
-            if constexpr (BITS == 2) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) w |= code[i][c] << (2 * i);
-                cimg[(k * TILE + 4 * tb) / 4] = (uint8_t)w;
-            } else {
-                uint32_t w = 0;
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) w |= code[i][c] << (4 * i);
-                *reinterpret_cast<uint16_t*>(cimg + (k * TILE + 4 * tb) / 2) = (uint16_t)w;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---------------- coalesced copy-out ----------------
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(cimg);
-        uint4* dst = reinterpret_cast<uint4*>(codes_out);
-        for (int k = tid; k < CODE_BYTES / 16; k += NT) dst[k] = src[k];
-        const uint4* msrc = reinterpret_cast<const uint4*>(mimg);
-        uint4* mdst = reinterpret_cast<uint4*>(meta_out);
-        for (int k = tid; k < META_HALVES / 8; k += NT) mdst[k] = msrc[k];
     }
 }
 
-// LDS floats needed: part [32][D] + colv/colv2 [2][D] + the K max buffer
-// [32][D] + 16 gauge partials; the code and meta images reuse the front.
+// LDS floats: partials [2D][17] float2 + colv/colv2 [2][D] + flag/pad 4 +
+// gauge 16; the V code exchange reuses the front.
 template <int D>
-constexpr int quant_lds_floats() { return 32 * D + 2 * D + 32 * D + 16; }
+constexpr int quant_lds_floats() { return 4 * (CPL + 1) * D + 2 * D + 4 + 16; }
 
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
-    __shared__ float lds[quant_lds_floats<D>()];
+    __shared__ __align__(16) float lds[quant_lds_floats<D>()];
     const int64_t tile = blockIdx.x;
     if (tile < args.n_k) {
         quantize_tile<D, KB, true>(args.k + tile * TILE * args.d0, args.d0, args.n_iters,
