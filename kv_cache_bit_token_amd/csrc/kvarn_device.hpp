@@ -83,12 +83,14 @@ template <> struct Net<16> {
 
 __device__ __forceinline__ float sign_of(int upper) { return upper ? -1.0f : 1.0f; }
 
-// Ordinary butterflies over the 16 in-lane channels of every token.
+// Ordinary butterflies over the 16 in-lane channels of every token, from
+// the stage of span H0 on (H0 = 2 when the loads already did the first).
+template <int H0 = 1>
 __device__ __forceinline__ void fwht_inlane(float (&x)[TPL][CPL]) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
 #pragma unroll
-        for (int h = 1; h < CPL; h <<= 1) {
+        for (int h = H0; h < CPL; h <<= 1) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 if ((c & h) == 0) {
@@ -192,6 +194,42 @@ __device__ __forceinline__ float rg_max(float v) {
     if constexpr (R >= 8) v = fmaxf(v, dpp<DPP_HMIR>(v));
     if constexpr (R >= 16) v = fmaxf(v, dpp<DPP_ROR8>(v));
     return v;
+}
+
+// First butterfly straight from a packed pair of fp16 values (lo, hi):
+// s = lo + hi, d = lo - hi, each with one fp32 rounding of the exact result
+// (the mixed-precision multiply-add widens both halves exactly), the same
+// values as widening first and adding in fp32.
+__device__ __forceinline__ void h2_butterfly(uint32_t w, float& s, float& d) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(s) : "v"(w));
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+}
+
+// Min / max across the R lanes of a row-group for four values at once, one
+// DPP instruction per value and stage (the s_nop gives the DPP read its two
+// wait states after the VALU write of the same VGPRs).  Inputs are results
+// of arithmetic, never signalling NaNs, so the plain min/max is exact.
+#define KVARN_DPP4(OP, CTRL)                                              \
+    asm volatile("s_nop 1\n"                                             \
+                 OP "_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+                 OP "_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+                 OP "_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+                 OP "_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]))
+
+template <int R, bool MAX>
+__device__ __forceinline__ void rg_minmax4(float (&v)[4]) {
+    if constexpr (MAX) {
+        KVARN_DPP4("v_max_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_max_f32", "quad_perm:[2,3,0,1]");
+        if constexpr (R >= 8) KVARN_DPP4("v_max_f32", "row_half_mirror");
+        if constexpr (R >= 16) KVARN_DPP4("v_max_f32", "row_ror:8");
+    } else {
+        KVARN_DPP4("v_min_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_min_f32", "quad_perm:[2,3,0,1]");
+        if constexpr (R >= 8) KVARN_DPP4("v_min_f32", "row_half_mirror");
+        if constexpr (R >= 16) KVARN_DPP4("v_min_f32", "row_ror:8");
+    }
 }
 
 // Flat-group test of the normalisation in fp32: a spread below 2^-16 of the

@@ -34,7 +34,7 @@
 //    cancels in its codes and folds back in SK, ZK: the kernel quantises
 //    X' * (1/R[t]) directly.  Likewise V quantises X' * (1/C[c]) and the row
 //    factor cancels, so V skips the last row pass (its result is not used).
-//  * A code is u = (v - z) / s rounded to the nearest integer, ties to even,
+//  * A code is u = (v - z) * (L / range) rounded to the nearest integer, ties to even,
 //    by the unsigned-byte conversion (which also clamps to [0, 255]), packed
 //    four to a register and merged with shifts.
 #include "kvarn_device.hpp"
@@ -48,7 +48,7 @@ __device__ __forceinline__ uint32_t cvt_u8(float u, uint32_t acc) {
     return __builtin_amdgcn_cvt_pk_u8_f32(u, SEL, acc);
 }
 
-template <int D, int BITS, bool IS_K>
+template <int D, int BITS, bool IS_K, bool FULL>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, int d0, int n_iters,
                                               uint8_t* __restrict__ codes_out,
                                               uint16_t* __restrict__ meta_out, float* lds) {
@@ -79,7 +79,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     int* flag = reinterpret_cast<int*>(colv2 + D);   // [1] column-pass fallback request
     float* gsum = colv2 + D + 4;                     // [16] gauge partials
 
-    // ---------------- load (one HBM read) + pad ----------------
+    // ---------------- load (one HBM read) + pad + first butterfly ----------------
+    // FULL: d0 == D, no padding channels
     float x[TPL][CPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
@@ -87,23 +88,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
             const int ch0 = 16 * nb + 8 * hlf;
-            if (ch0 + 8 <= d0) {
-                uint4 w = *reinterpret_cast<const uint4*>(row + ch0);
-                uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            uint4 w = make_uint4(0u, 0u, 0u, 0u);
+            if (FULL || ch0 + 8 <= d0) w = *reinterpret_cast<const uint4*>(row + ch0);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    x[i][8 * hlf + 2 * k] = h2f_bits((uint16_t)(ws[k] & 0xFFFF));
-                    x[i][8 * hlf + 2 * k + 1] = h2f_bits((uint16_t)(ws[k] >> 16));
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) x[i][8 * hlf + k] = 0.0f;
-            }
+            for (int k = 0; k < 4; ++k)
+                h2_butterfly(ws[k], x[i][8 * hlf + 2 * k], x[i][8 * hlf + 2 * k + 1]);
         }
     }
 
     // ---------------- rotation (unscaled) ----------------
-    fwht_inlane(x);
+    fwht_inlane<2>(x);
     fwht_crosslane<R>(x, cb);
 
     // ---------------- normalisation ----------------
@@ -276,8 +271,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             mn = fminf(mn, dpp<DPP_XOR1>(mn));
             mx = fmaxf(mx, dpp<DPP_XOR1>(mx));
             const float zk = mn;
-            const float sk = (mx - mn) / (float)L;
-            const float inv = (mx > mn) ? 1.0f / sk : 0.0f;
+            const float range = mx - mn;
+            const float sk = range * (1.0f / (float)L);
+            const float inv = (range > 0.0f) ? (float)L * __builtin_amdgcn_rcpf(range) : 0.0f;
             if (rh == 0) {
                 colv[rp] = inv;
                 colv2[rp] = -zk * inv;
@@ -322,21 +318,26 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         }
     } else {
         // V: one group per token, over the D channels: values v = x * b[c]
-        float inv[TPL], off[TPL];
+        float inv[TPL], off[TPL], mn[TPL], mx[TPL];
         uint32_t sv2[TPL / 2], zv2[TPL / 2];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) x[i][c] *= b[c];
-            float mn = x[i][0], mx = x[i][0];
+            mn[i] = x[i][0];
+            mx[i] = x[i][0];
 #pragma unroll
-            for (int c = 1; c < CPL; ++c) { mn = fminf(mn, x[i][c]); mx = fmaxf(mx, x[i][c]); }
-            mn = rg_min<R>(mn);
-            mx = rg_max<R>(mx);
-            const float sv = (mx - mn) / (float)L;
-            inv[i] = (mx > mn) ? 1.0f / sv : 0.0f;
-            off[i] = -mn * inv[i];
-            const uint32_t hs = f2h_bits(sv * G), hz = f2h_bits(mn * G);
+            for (int c = 1; c < CPL; ++c) { mn[i] = fminf(mn[i], x[i][c]); mx[i] = fmaxf(mx[i], x[i][c]); }
+        }
+        rg_minmax4<R, false>(mn);
+        rg_minmax4<R, true>(mx);
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const float range = mx[i] - mn[i];
+            const float sv = range * (1.0f / (float)L);
+            inv[i] = (range > 0.0f) ? (float)L * __builtin_amdgcn_rcpf(range) : 0.0f;
+            off[i] = -mn[i] * inv[i];
+            const uint32_t hs = f2h_bits(sv * G), hz = f2h_bits(mn[i] * G);
             if (i & 1) { sv2[i / 2] |= hs << 16; zv2[i / 2] |= hz << 16; }
             else       { sv2[i / 2] = hs;        zv2[i / 2] = hz; }
         }
@@ -434,17 +435,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
 template <int D>
 constexpr int quant_lds_floats() { return 4 * (CPL + 1) * D + 2 * D + 4 + 16; }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool FULL>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
     __shared__ __align__(16) float lds[quant_lds_floats<D>()];
     const int64_t tile = blockIdx.x;
     if (tile < args.n_k) {
-        quantize_tile<D, KB, true>(args.k + tile * TILE * args.d0, args.d0, args.n_iters,
+        quantize_tile<D, KB, true, FULL>(args.k + tile * TILE * args.d0, args.d0, args.n_iters,
                                    args.kc + tile * (TILE * D * KB / 8),
                                    args.km + tile * (2 * D + TILE), lds);
     } else {
         const int64_t vt = tile - args.n_k;
-        quantize_tile<D, VB, false>(args.v + vt * TILE * args.d0, args.d0, args.n_iters,
+        quantize_tile<D, VB, false, FULL>(args.v + vt * TILE * args.d0, args.d0, args.n_iters,
                                     args.vc + vt * (TILE * D * VB / 8),
                                     args.vm + vt * (2 * TILE + D), lds);
     }
@@ -453,7 +454,10 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
 template <int D, int KB, int VB>
 static hipError_t launch_q(const QuantArgs& a, hipStream_t s) {
     const int64_t blocks = a.n_k + a.n_v;
-    hipLaunchKernelGGL((quantize_kernel<D, KB, VB>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
+    if (a.d0 == D)
+        hipLaunchKernelGGL((quantize_kernel<D, KB, VB, true>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
+    else
+        hipLaunchKernelGGL((quantize_kernel<D, KB, VB, false>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
     return hipGetLastError();
 }
 
