@@ -9,11 +9,16 @@
 // back to the original channels; the first head_dim channels are rounded to
 // fp16 (nearest even).
 //
-// One workgroup = one tile, 2*D threads, same register layout and transform
-// network as the quantiser (kvarn_device.hpp).  The packed codes and meta
-// of the tile are copied into LDS with 16-byte loads, each lane then reads
-// its 4 tokens x 16 channels, transforms in registers and stores 32 bytes per
-// token.  The per-token K factor RK_t and the 1/sqrt(D) scale are applied
+// 2*D threads per workgroup, same register layout and transform network as
+// the quantiser (kvarn_device.hpp).  A workgroup walks a strided sequence of
+// tiles (K tiles or V tiles) and loads the packed codes and meta of the next
+// tile into registers while it transforms the current one, so the HBM
+// latency of the (small) packed input overlaps the arithmetic.  Each lane
+// reads exactly the bytes it needs: K codes are token-major, so a lane's 16
+// channels of one token are one 8- (4-bit) or 4-byte (2-bit) word; V codes
+// are channel-major, so lanes holding neighbouring token groups load whole
+// words of their channel rows and swap bytes through LDS inside the
+// wavefront.  The per-token K factor RK_t and the 1/sqrt(D) scale are applied
 // after the transform (they commute with it); for V, 1/sqrt(D) is folded
 // into CV_j.
 #include "kvarn_device.hpp"
@@ -21,95 +26,188 @@
 
 namespace kvarn {
 
-template <int D, int BITS, bool IS_K>
-__device__ __forceinline__ void dequantize_tile(const uint8_t* __restrict__ codes_in,
-                                                const uint16_t* __restrict__ meta_in, int d0,
-                                                uint16_t* __restrict__ out, uint32_t* lds) {
-    constexpr int R = D / CPL;
-    constexpr int NT = 2 * D;
-    constexpr int CODE_BYTES = TILE * D * BITS / 8;
-    constexpr int META_HALVES = IS_K ? 2 * D + TILE : 2 * TILE + D;
-    constexpr uint32_t MASK = (1u << BITS) - 1;
-    using N = Net<R>;
+// Per-wavefront LDS region (2048 words): [0, 512) the V byte swap,
+// [1536, 1536 + 4 * NC) the tile's meta as the wave needs it, and all of it
+// for the output staging once both have been read.
+constexpr int kWaveWords = 2048;
+constexpr int kMetaWord = 1536;
 
-    const int tid = threadIdx.x;
-    const int cb = tid % R;
-    const int tb = tid / R;
-    const int nb = cb ^ N::kF;   // rotated channel block read by this lane
-    const int ob = N::nu(cb);    // output channel block held after the transform
-    const float rsqrtD = 1.0f / __builtin_sqrtf((float)D);
-
-    // ---- stage the packed tile in LDS ----
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(codes_in);
-        uint4* dst = reinterpret_cast<uint4*>(lds);
-        for (int k = tid; k < CODE_BYTES / 16; k += NT) dst[k] = src[k];
-        const uint4* msrc = reinterpret_cast<const uint4*>(meta_in);
-        uint4* mdst = reinterpret_cast<uint4*>(lds + CODE_BYTES / 4);
-        for (int k = tid; k < META_HALVES / 8; k += NT) mdst[k] = msrc[k];
+// Meta of one tile for one wavefront of TW = 4096 / D tokens, gathered by
+// the wave's lanes as 16-byte chunks (one global load per lane instead of
+// every lane fetching its own copies):
+//   K: SK (D halves) | ZK (D halves) | RK of the wave's tokens (TW halves)
+//   V: SV of the wave's tokens | ZV of the wave's tokens | CV (D halves)
+template <int D, bool IS_K>
+struct MetaPlan {
+    static constexpr int TW = 4096 / D;
+    static constexpr int NC = IS_K ? D / 4 + TW / 8 : TW / 4 + D / 8;   // chunks
+    static constexpr int NS = (NC + 63) / 64;                            // per lane
+    // source offset (halves, within the tile's meta) of chunk e; tok0 =
+    // first token of the wave
+    __device__ static int src(int e, int tok0) {
+        if (IS_K) return e < D / 4 ? 8 * e : 2 * D + tok0 + 8 * (e - D / 4);
+        if (e < TW / 8) return tok0 + 8 * e;
+        if (e < TW / 4) return TILE + tok0 + 8 * (e - TW / 8);
+        return 2 * TILE + 8 * (e - TW / 4);
     }
-    __syncthreads();
-    const uint8_t* cimg = reinterpret_cast<const uint8_t*>(lds);
-    const uint16_t* mimg = reinterpret_cast<const uint16_t*>(lds + CODE_BYTES / 4);
+};
 
-    // ---- unpack my 4 tokens x 16 channels ----
-    float code[TPL][CPL];
+// packed inputs of one tile held by one lane
+template <int D, int BITS, bool IS_K> struct Packed;
+template <int D, int BITS> struct Packed<D, BITS, true> {
+    uint32_t c[TPL][BITS / 2];           // token 4*tb + i: 16 channels of block nb
+    uint4 m[MetaPlan<D, true>::NS];      // meta chunks
+};
+template <int D, int BITS> struct Packed<D, BITS, false> {
+    uint32_t g[BITS == 2 ? 4 : 8];       // words of channel rows (before the in-wave swap)
+    uint4 m[MetaPlan<D, false>::NS];
+};
+
+__device__ __forceinline__ float half_of(const uint32_t* pairs, int k) {
+    return h2f_bits((uint16_t)((k & 1) ? (pairs[k >> 1] >> 16) : (pairs[k >> 1] & 0xFFFF)));
+}
+__device__ __forceinline__ void lds16(uint32_t* dst, const uint32_t* src) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 4);
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+}
+
+template <int D, int BITS, bool IS_K>
+__device__ __forceinline__ void load_tile(Packed<D, BITS, IS_K>& p, const uint8_t* __restrict__ codes,
+                                          const uint16_t* __restrict__ meta, int tb, int nb) {
+    using MP = MetaPlan<D, IS_K>;
+    const int ln = threadIdx.x & 63;
+    const int tok0 = (threadIdx.x >> 6) * MP::TW;
+#pragma unroll
+    for (int k = 0; k < MP::NS; ++k) {
+        int e = ln + 64 * k;
+        if (e >= MP::NC) e = 0;   // spare lanes re-read chunk 0 (keeps the load unconditional)
+        p.m[k] = *reinterpret_cast<const uint4*>(meta + MP::src(e, tok0));
+    }
     if constexpr (IS_K) {
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            const int t = 4 * tb + i;
+            const uint8_t* src = codes + ((4 * tb + i) * D + 16 * nb) * BITS / 8;
             if constexpr (BITS == 4) {
-                const uint2 w = *reinterpret_cast<const uint2*>(cimg + (t * D + 16 * nb) / 2);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    code[i][c] = (float)((w.x >> (4 * c)) & MASK);
-                    code[i][8 + c] = (float)((w.y >> (4 * c)) & MASK);
-                }
+                const uint2 w = *reinterpret_cast<const uint2*>(src);
+                p.c[i][0] = w.x;
+                p.c[i][1] = w.y;
             } else {
-                const uint32_t w = *reinterpret_cast<const uint32_t*>(cimg + (t * D + 16 * nb) / 4);
-#pragma unroll
-                for (int c = 0; c < 16; ++c) code[i][c] = (float)((w >> (2 * c)) & MASK);
+                p.c[i][0] = *reinterpret_cast<const uint32_t*>(src);
             }
         }
     } else {
+        constexpr int ROWB = TILE * BITS / 8;   // bytes per channel row
+        if constexpr (BITS == 2) {
+            const int m = tb >> 2, j = tb & 3;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int k = 16 * nb + c;
-            uint32_t w;
-            if constexpr (BITS == 2) w = cimg[(k * TILE + 4 * tb) / 4];
-            else w = *reinterpret_cast<const uint16_t*>(cimg + (k * TILE + 4 * tb) / 2);
+            for (int n = 0; n < 4; ++n)
+                p.g[n] = *reinterpret_cast<const uint32_t*>(codes + (16 * nb + 4 * j + n) * ROWB + 4 * m);
+        } else {
+            const int m = tb >> 1, j = tb & 1;
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) code[i][c] = (float)((w >> (BITS * i)) & MASK);
+            for (int q = 0; q < 8; ++q)
+                p.g[q] = *reinterpret_cast<const uint32_t*>(codes + (16 * nb + 2 * q + j) * ROWB + 4 * m);
         }
     }
+}
 
-    // ---- folded scales -> rotated-domain values ----
+template <int D, int BITS, bool IS_K, bool FULL>
+__device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, int d0,
+                                                uint16_t* __restrict__ out, uint32_t* xch) {
+    constexpr int R = D / CPL;
+    constexpr uint32_t MASK = (1u << BITS) - 1;
+    using N = Net<R>;
+    using MP = MetaPlan<D, IS_K>;
+    const int tid = threadIdx.x;
+    const int cb = tid % R;
+    const int tb = tid / R;
+    const int ln = tid & 63;
+    const int tbl = ln / R;                 // token group within the wave
+    const int nb = cb ^ N::kF;             // rotated channel block read by this lane
+    const int ob = N::nu(cb);              // output channel block held after the transform
+    const float rsqrtD = 1.0f / __builtin_sqrtf((float)D);
+    uint32_t* mw = xch + kMetaWord;        // the wave's meta words (2 halves each)
+
+    wave_sync();   // the previous tile's reads of this wave's LDS are done
+#pragma unroll
+    for (int k = 0; k < MP::NS; ++k)
+        if (ln + 64 * k < MP::NC) *reinterpret_cast<uint4*>(mw + 4 * (ln + 64 * k)) = p.m[k];
+
     float x[TPL][CPL];
     float rowscale[TPL];
     if constexpr (IS_K) {
-        float sk[CPL], zk[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            sk[c] = h2f_bits(mimg[16 * nb + c]);
-            zk[c] = h2f_bits(mimg[D + 16 * nb + c]);
-        }
+        wave_sync();
+        uint32_t sk[8], zk[8], rk[2];
+        lds16(sk, mw + 8 * nb);
+        lds16(zk, mw + D / 2 + 8 * nb);
+        const uint2 r2 = *reinterpret_cast<const uint2*>(mw + D + 2 * tbl);
+        rk[0] = r2.x;
+        rk[1] = r2.y;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            rowscale[i] = h2f_bits(mimg[2 * D + 4 * tb + i]) * rsqrtD;
+            rowscale[i] = half_of(rk, i) * rsqrtD;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) x[i][c] = __builtin_fmaf(code[i][c], sk[c], zk[c]);
+            for (int c = 0; c < CPL; ++c) {
+                const uint32_t w = (BITS == 4) ? p.c[i][c >> 3] : p.c[i][0];
+                const int sh = (BITS == 4) ? 4 * (c & 7) : 2 * c;
+                const float code = (float)((w >> sh) & MASK);
+                x[i][c] = __builtin_fmaf(code, half_of(sk, c), half_of(zk, c));
+            }
         }
     } else {
+        // in-wave swap: lane (token group tb) gets word q = channels of its block
+        // (2-bit: 4 channels 4q..4q+3, a byte each; 4-bit: channels 2q, 2q+1, two bytes each)
+        constexpr int NW = BITS == 2 ? 4 : 8;
+        uint32_t w[NW];
+        if constexpr (BITS == 2) {
+            const uint32_t A = __builtin_amdgcn_perm(p.g[1], p.g[0], 0x05010400u);
+            const uint32_t B = __builtin_amdgcn_perm(p.g[1], p.g[0], 0x07030602u);
+            const uint32_t C = __builtin_amdgcn_perm(p.g[3], p.g[2], 0x05010400u);
+            const uint32_t E = __builtin_amdgcn_perm(p.g[3], p.g[2], 0x07030602u);
+            *reinterpret_cast<uint4*>(xch + 4 * ln) =
+                make_uint4(__builtin_amdgcn_perm(C, A, 0x05040100u), __builtin_amdgcn_perm(C, A, 0x07060302u),
+                           __builtin_amdgcn_perm(E, B, 0x05040100u), __builtin_amdgcn_perm(E, B, 0x07060302u));
+            wave_sync();
+            const int j = tb & 3;
+            const int base = ln - j * R;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = xch[4 * (base + q * R) + j];
+        } else {
+            *reinterpret_cast<uint4*>(xch + 8 * ln) = make_uint4(p.g[0], p.g[1], p.g[2], p.g[3]);
+            *reinterpret_cast<uint4*>(xch + 8 * ln + 4) = make_uint4(p.g[4], p.g[5], p.g[6], p.g[7]);
+            wave_sync();
+            const int j = tb & 1;
+            const int base = ln - j * R;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t r0 = xch[8 * base + q], r1 = xch[8 * (base + R) + q];
+                w[q] = j ? __builtin_amdgcn_perm(r1, r0, 0x07060302u) : __builtin_amdgcn_perm(r1, r0, 0x05040100u);
+            }
+        }
+        uint32_t sv[2], zv[2], cvw[8];
+        {
+            const uint2 s2 = *reinterpret_cast<const uint2*>(mw + 2 * tbl);
+            const uint2 z2 = *reinterpret_cast<const uint2*>(mw + MP::TW / 2 + 2 * tbl);
+            sv[0] = s2.x; sv[1] = s2.y;
+            zv[0] = z2.x; zv[1] = z2.y;
+            lds16(cvw, mw + MP::TW + 8 * nb);
+        }
         float cv[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) cv[c] = h2f_bits(mimg[2 * TILE + 16 * nb + c]) * rsqrtD;
+        for (int c = 0; c < CPL; ++c) cv[c] = half_of(cvw, c) * rsqrtD;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            const float sv = h2f_bits(mimg[4 * tb + i]);
-            const float zv = h2f_bits(mimg[TILE + 4 * tb + i]);
+            const float svi = half_of(sv, i), zvi = half_of(zv, i);
             rowscale[i] = 1.0f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) x[i][c] = cv[c] * __builtin_fmaf(code[i][c], sv, zv);
+            for (int c = 0; c < CPL; ++c) {
+                const uint32_t word = (BITS == 2) ? w[c >> 2] : w[c >> 1];
+                const int sh = (BITS == 2) ? 8 * (c & 3) + 2 * i : 16 * (c & 1) + 4 * i;
+                const float code = (float)((word >> sh) & MASK);
+                x[i][c] = cv[c] * __builtin_fmaf(code, svi, zvi);
+            }
         }
     }
 
@@ -117,47 +215,134 @@ __device__ __forceinline__ void dequantize_tile(const uint8_t* __restrict__ code
     fwht_inlane(x);
     fwht_crosslane<R>(x, cb);
 
-    // ---- fp16 store of the first d0 channels ----
-    if (16 * ob < d0) {
+    // ---- fp16 store ----
+    if constexpr (FULL) {
+        // d0 == D: the wave's 256/R tokens are one contiguous 8 KB run of the
+        // output.  Stage it in the wave's LDS region (16-byte chunks, chunk
+        // index flipped in its lowest bit by token-group parity and by the
+        // upper half of a 512-byte row, so the staging writes of a quarter
+        // wave fall on distinct banks) and store it with fully contiguous
+        // 1 KB wave stores.  The store count is fixed, so the wait for the
+        // next tile's loads need not cover these stores.
+        constexpr int CPR = D / 8;   // 16-byte chunks per token row
+        const int ln = tid & 63;
+        wave_sync();
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            uint32_t w[8];
+            const int r = 4 * (ln / R) + i;   // row within the wave's run
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = f2h_bits(x[i][8 * h + 2 * k] * rowscale[i]);
+                    const uint32_t hi = f2h_bits(x[i][8 * h + 2 * k + 1] * rowscale[i]);
+                    o[k] = lo | (hi << 16);
+                }
+                const int ch = 2 * ob + h;
+                const int phys = r * CPR + (ch ^ (((r >> 2) ^ (ch >> 4)) & 1));
+                *reinterpret_cast<uint4*>(xch + 4 * phys) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        wave_sync();
+        uint4* dst = reinterpret_cast<uint4*>(out + (size_t)(tid >> 6) * (256 / R) * D);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const int g = ln + 64 * s2;
+            const int r = g / CPR, ch = g % CPR;
+            const int phys = r * CPR + (ch ^ (((r >> 2) ^ (ch >> 4)) & 1));
+            dst[g] = *reinterpret_cast<const uint4*>(xch + 4 * phys);
+        }
+    } else if (16 * ob < d0) {
+        // padded head_dim: the first d0 channels, straight from registers
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            uint32_t o[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t lo = f2h_bits(x[i][2 * k] * rowscale[i]);
                 const uint32_t hi = f2h_bits(x[i][2 * k + 1] * rowscale[i]);
-                w[k] = lo | (hi << 16);
+                o[k] = lo | (hi << 16);
             }
             uint16_t* dst = out + (size_t)(4 * tb + i) * d0 + 16 * ob;
-            *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-            if (16 * ob + 16 <= d0) *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (16 * ob + 16 <= d0) *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
         }
     }
 }
 
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs args) {
-    constexpr int KBYTES = TILE * D * KB / 8 + 2 * (2 * D + TILE);
-    constexpr int VBYTES = TILE * D * VB / 8 + 2 * (2 * TILE + D);
-    constexpr int WORDS = (KBYTES > VBYTES ? KBYTES : VBYTES) / 4;
-    __shared__ uint32_t lds[WORDS];
-    const int64_t tile = blockIdx.x;
-    if (tile < args.n_k) {
-        dequantize_tile<D, KB, true>(args.kc + tile * (TILE * D * KB / 8),
-                                     args.km + tile * (2 * D + TILE), args.d0,
-                                     args.ko + tile * TILE * args.d0, lds);
-    } else {
-        const int64_t vt = tile - args.n_k;
-        dequantize_tile<D, VB, false>(args.vc + vt * (TILE * D * VB / 8),
-                                      args.vm + vt * (2 * TILE + D), args.d0,
-                                      args.vo + vt * TILE * args.d0, lds);
+// Tiles first, first + stride, ... of one tensor, the next tile's packed
+// input in flight while the current one is transformed.
+template <int D, int BITS, bool IS_K, bool FULL>
+__device__ __forceinline__ void dequantize_run(const uint8_t* __restrict__ codes,
+                                               const uint16_t* __restrict__ meta,
+                                               uint16_t* __restrict__ out, int64_t n, int64_t first,
+                                               int64_t stride, int d0, uint32_t* xch) {
+    constexpr int R = D / CPL;
+    constexpr int64_t CB = TILE * D * BITS / 8;                     // code bytes per tile
+    constexpr int64_t MH = IS_K ? 2 * D + TILE : 2 * TILE + D;      // meta halves per tile
+    const int tid = threadIdx.x;
+    const int cb = tid % R;
+    const int tb = tid / R;
+    const int nb = cb ^ Net<R>::kF;   // rotated channel block read by this lane
+    // The prefetch is unconditional (the last one re-reads the current
+    // tile) so that the wait before each tile covers exactly one tile's loads.
+    Packed<D, BITS, IS_K> cur, nxt;
+    int64_t t = first;
+    load_tile<D, BITS, IS_K>(cur, codes + t * CB, meta + t * MH, tb, nb);
+    // Wait for the first tile here, once: the loop then starts every tile
+    // with no loads pending into the current registers, and the only wait
+    // per tile is for the prefetched loads, issued before its stores.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (;;) {
+        const int64_t tn = (t + stride < n) ? t + stride : t;
+        load_tile<D, BITS, IS_K>(nxt, codes + tn * CB, meta + tn * MH, tb, nb);
+        dequantize_tile<D, BITS, IS_K, FULL>(cur, d0, out + t * TILE * d0, xch + (threadIdx.x >> 6) * kWaveWords);
+        t += stride;
+        if (t >= n) break;
+        cur = nxt;
     }
 }
 
+template <int D, int KB, int VB, bool FULL>
+__global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs args, int64_t gk) {
+    __shared__ __align__(16) uint32_t xch[(2 * D / 64) * kWaveWords];
+    const int64_t b = blockIdx.x;
+    if (b < gk) {
+        dequantize_run<D, KB, true, FULL>(args.kc, args.km, args.ko, args.n_k, b, gk, args.d0, xch);
+    } else {
+        dequantize_run<D, VB, false, FULL>(args.vc, args.vm, args.vo, args.n_v, b - gk,
+                                     (int64_t)gridDim.x - gk, args.d0, xch);
+    }
+}
+
+// Grid: as many workgroups as fit on the device at once (at most one per
+// tile), split between K and V in proportion to their tile counts.
 template <int D, int KB, int VB>
 static hipError_t launch_dq(const DequantArgs& a, hipStream_t s) {
-    const int64_t blocks = a.n_k + a.n_v;
-    hipLaunchKernelGGL((dequantize_kernel<D, KB, VB>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
+    auto kern = (a.d0 == D) ? dequantize_kernel<D, KB, VB, true> : dequantize_kernel<D, KB, VB, false>;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 2 * D, 0);
+    if (e != hipSuccess) return e;
+    const int64_t total = a.n_k + a.n_v;
+    const int64_t parts = (a.n_k > 0) + (a.n_v > 0);
+    int64_t g = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    if (g > total) g = total;
+    if (g < parts) g = parts;
+    int64_t gk = 0, gv = 0;
+    if (a.n_k > 0) {
+        gk = (g * a.n_k + total / 2) / total;
+        if (gk < 1) gk = 1;
+        if (a.n_v > 0 && gk > g - 1) gk = g - 1;
+        if (gk > a.n_k) gk = a.n_k;
+    }
+    if (a.n_v > 0) {
+        gv = g - gk;
+        if (gv > a.n_v) gv = a.n_v;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(gk + gv)), dim3(2 * D), 0, s, a, gk);
     return hipGetLastError();
 }
 
