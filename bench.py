@@ -14,9 +14,25 @@ the quantiser, produced by the dequantiser and represented by the cache the
 attention reads) per second.  Per-stage times come from HIP events recorded on
 the stream the kernels run on.
 
+The roofline object covers the dominant kernel, the quantiser.  Its bound is
+the vector ALU, not HBM: at 5 iterations the method needs about 40
+fp32 operations per element (quant_ops_per_elem below) against a 2-byte input
+element, far above the HBM balance point.  `achieved` is those algorithmic
+operations per second over the kernel's HIP-event time, `peak` the issue rate
+of the fp32 VALUs (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one operation per
+lane per cycle; packed two-wide fp32 instructions are not used), and the
+stage table keeps every kernel's HBM fraction.  `traffic` is the quantiser's
+measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+plain device-to-device copy of known size), recorded for the kernel source
+whose SHA-256 prefix is stored beside it; it reads null once the source
+differs.
+
 Prints one JSON line.  `--gpus` above 1 exits: this build runs on one GPU.
+`--copy-calibration` instead runs a plain 1 GiB device copy (the reference
+for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,8 +42,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+VALU_PEAK = 256 * 4 * 16 * 2.4e9   # fp32 VALU lane operations/s (CUs x SIMDs x lanes x clock)
 LAYERS, KV_HEADS, TOKENS, HEAD_DIM, Q_HEADS = 64, 8, 16384, 128, 32
 K_BITS, V_BITS, N_ITERS = 4, 2, 5
+
+
+def quant_ops_per_elem(D, n_iters):
+    """Algorithmic fp32 operations per element of the quantiser (K and V mean).
+
+    rotation log2(D) butterflies; each standard-deviation pass scales the
+    element by the cross-axis factor, adds it and accumulates its square (3);
+    K runs 2*n_iters passes, V 2*n_iters - 1 (its last row factor cancels in
+    its per-token groups); the quantiser scales the element into its group,
+    takes min and max, and applies the affine map and the rounding (5).
+    """
+    lg = D.bit_length() - 1
+    k = lg + 3 * 2 * n_iters + 5
+    v = lg + 3 * (2 * n_iters - 1) + 5
+    return (k + v) / 2
+
+
+# HBM bytes per launch of the quantiser on this workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE (scaled by the copy calibration), and the SHA-256
+# prefix of the kernel source they were taken for.
+QUANT_TRAFFIC = {"source_sha256": "6920e17daa51c78e", "fetch_bytes": 4295772351, "write_bytes": 905969664}
+QUANT_SOURCE = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", "kvarn_quantize.hip")
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def per_tile_bytes(D):
@@ -39,34 +83,60 @@ def per_tile_bytes(D):
     return {"fp16_pair": 2 * fp16, "packed_pair": kc + vc + km + vm}
 
 
-def cpu_baseline(k, v, q, n_seq):
-    """The oracle, untuned, on the first n_seq (layer, head) sequences."""
-    import numpy as np
+def cpu_baseline(k, v, q, n_seq, chunk=32):
+    """The oracle, untuned, on the first n_seq (layer, head) sequences, fed in
+    chunks of `chunk` sequences (only the oracle calls are timed)."""
     import oracle
 
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     tiles_per_seq = TOKENS // 128
+    kt_all = k.view(-1, 128, HEAD_DIM)
+    vt_all = v.view(-1, 128, HEAD_DIM)
+    dt = 0.0
+    for s0 in range(0, n_seq, chunk):
+        s1 = min(n_seq, s0 + chunk)
+        kt = kt_all[s0 * tiles_per_seq:s1 * tiles_per_seq].cpu().numpy()
+        vt = vt_all[s0 * tiles_per_seq:s1 * tiles_per_seq].cpu().numpy()
+        # the query heads of the (layer, head) sequences in this chunk
+        layers = sorted({s // KV_HEADS for s in range(s0, s1)})
+        t0 = time.perf_counter()
+        qk = oracle.quantize_tiles(kt, K_BITS, N_ITERS, True)
+        qv = oracle.quantize_tiles(vt, V_BITS, N_ITERS, False)
+        oracle.dequantize_tiles(qk["codes"], qk["meta"], HEAD_DIM, K_BITS, True)
+        oracle.dequantize_tiles(qv["codes"], qv["meta"], HEAD_DIM, V_BITS, False)
+        dt += time.perf_counter() - t0
+        for layer in layers:
+            g0, g1 = max(s0, layer * KV_HEADS), min(s1, (layer + 1) * KV_HEADS)
+            sl = slice((g0 - s0) * tiles_per_seq, (g1 - s0) * tiles_per_seq)
+            g = (g0 % KV_HEADS, g1 - g0)
+            qh = q[layer:layer + 1, g[0] * (Q_HEADS // KV_HEADS):(g[0] + g[1]) * (Q_HEADS // KV_HEADS)]
+            qh = qh.cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.decode_attention(qh, qk["codes"][sl], qv["codes"][sl], qk["meta"][sl], qv["meta"][sl],
+                                    n_kv_heads=g[1], tiles_per_seq=tiles_per_seq,
+                                    k_bits=K_BITS, v_bits=V_BITS)
+            dt += time.perf_counter() - t0
+        del qk, qv, kt, vt
     n_tiles = n_seq * tiles_per_seq
-    kt = k.view(-1, 128, HEAD_DIM)[:n_tiles].cpu().numpy()
-    vt = v.view(-1, 128, HEAD_DIM)[:n_tiles].cpu().numpy()
-    n_layers = n_seq // KV_HEADS
-    qh = q[:n_layers].cpu().numpy()
-    t0 = time.perf_counter()
-    qk = oracle.quantize_tiles(kt, K_BITS, N_ITERS, True)
-    qv = oracle.quantize_tiles(vt, V_BITS, N_ITERS, False)
-    oracle.dequantize_tiles(qk["codes"], qk["meta"], HEAD_DIM, K_BITS, True)
-    oracle.dequantize_tiles(qv["codes"], qv["meta"], HEAD_DIM, V_BITS, False)
-    oracle.decode_attention(qh, qk["codes"], qv["codes"], qk["meta"], qv["meta"],
-                            n_kv_heads=KV_HEADS, tiles_per_seq=tiles_per_seq,
-                            k_bits=K_BITS, v_bits=V_BITS)
-    dt = time.perf_counter() - t0
     fp16_bytes = 3 * n_tiles * per_tile_bytes(HEAD_DIM)["fp16_pair"]
-    return {"value": fp16_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(fp16_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": "%d of %d (layer, head) sequences (%d tile pairs): quantize + dequantize "
-                      "+ decode attention of their %d query heads, fp64 oracle" % (
-                          n_seq, LAYERS * KV_HEADS, n_tiles, n_layers * Q_HEADS)}
+                      "+ decode attention of their query heads, fp64 oracle, same inputs and unit "
+                      "as value" % (n_seq, LAYERS * KV_HEADS, n_tiles)}
+
+
+def copy_calibration():
+    """Plain device-to-device copy of exactly 1 GiB (read 1 GiB, write 1 GiB)."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def main():
@@ -74,9 +144,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=128,
+    ap.add_argument("--cpu-seqs", type=int, default=LAYERS * KV_HEADS,
                     help="(layer, head) sequences in the CPU-oracle sample; 0 skips it")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the KVarN path on one GPU only; "
               "--gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
@@ -151,8 +226,14 @@ def main():
                         "hbm_frac": round(gbs / HBM_PEAK, 4),
                         "fp16_equiv_GBps": round(fp16_total / (ms / 1e3) / 1e9, 1),
                         "tile_pairs_per_s": round(n_tiles / (ms / 1e3), 0)}
-    dom = max(stages, key=lambda s: stages[s]["ms"])
-    achieved = hbm[dom] / (stages[dom]["ms"] / 1e3)
+    # roofline of the quantiser (the dominant kernel): vector-ALU bound
+    q_ms = stages["quantize"]["ms"]
+    elems = n_tiles * 2 * 128 * HEAD_DIM
+    q_ops = quant_ops_per_elem(HEAD_DIM, N_ITERS) * elems
+    achieved = q_ops / (q_ms / 1e3)
+    traffic = None
+    if QUANT_TRAFFIC["source_sha256"] == source_sha(QUANT_SOURCE):
+        traffic = QUANT_TRAFFIC["fetch_bytes"] + QUANT_TRAFFIC["write_bytes"]
     result = {
         "metric": "KV GB/s quantized/dequantized (fp16 in) and % of HBM peak, K4V2 g128",
         "value": round(3 * fp16_total / (ms_step / 1e3) / 1e9, 2),
@@ -166,9 +247,12 @@ def main():
                                "5 iterations, GQA 32/8",
                    "tiles": n_tiles, "kv_fp16_bytes": fp16_total, "packed_bytes": packed_total},
         "stages": stages,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1),
-                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None},
+        "roofline": {"kernel": "quantize", "bound": "alu", "achieved": round(achieved / 1e12, 3),
+                     "peak": round(VALU_PEAK / 1e12, 3), "unit": "Top/s",
+                     "frac": round(achieved / VALU_PEAK, 4), "traffic": traffic,
+                     "ops_per_elem": quant_ops_per_elem(HEAD_DIM, N_ITERS),
+                     "algorithmic_hbm_bytes": hbm["quantize"],
+                     "hbm_frac": stages["quantize"]["hbm_frac"]},
         "wall_s": round(t_wall, 3),
     }
     if args.cpu_seqs > 0:
