@@ -154,14 +154,14 @@ template <int D>
 struct AttnLds {
     static constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
     static constexpr int NKB = D / 16;
-    __host__ __device__ static int kmeta(int) { return 0; }
-    __host__ __device__ static int vmeta(int) { return 2 * KMH; }
-    __host__ __device__ static int bq(int) { return 2 * KMH + 2 * VMH; }
-    __host__ __device__ static int sc(int G) { return bq(G) + 64 * G * NKB; }
-    __host__ __device__ static int pa(int G) { return sc(G) + 512 * G; }
-    __host__ __device__ static int pvc(int G) { return pa(G) + 512 * G; }
-    __host__ __device__ static int stats(int G) { return pvc(G) + 4 * D * ((G + 3) & ~3); }
-    __host__ __device__ static int bytes(int G) { return stats(G) + 16 * G + 16; }
+    __host__ __device__ static constexpr int kmeta(int) { return 0; }
+    __host__ __device__ static constexpr int vmeta(int) { return 2 * KMH; }
+    __host__ __device__ static constexpr int bq(int) { return 2 * KMH + 2 * VMH; }
+    __host__ __device__ static constexpr int sc(int G) { return bq(G) + 64 * G * NKB; }
+    __host__ __device__ static constexpr int pa(int G) { return sc(G) + 512 * G; }
+    __host__ __device__ static constexpr int pvc(int G) { return pa(G) + 512 * G; }
+    __host__ __device__ static constexpr int stats(int G) { return pvc(G) + 4 * D * ((G + 3) & ~3); }
+    __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * G + 16; }
 };
 
 template <int D, int KB, int VB, int GMAX>
@@ -260,20 +260,19 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int n = 0; n < GMAX; ++n) acc[r][n] = 0.0f;
 
-    // MFMA operands built from the per-tile images (zero rows for n >= G)
-    h4_t bq_hi[NKB], bq_lo[NKB], pa_hi[NVB], pa_lo[NVB];
-#pragma unroll
-    for (int k = 0; k < NKB; ++k) { bq_hi[k] = (h4_t){0, 0, 0, 0}; bq_lo[k] = bq_hi[k]; }
-#pragma unroll
-    for (int k = 0; k < NVB; ++k) { pa_hi[k] = (h4_t){0, 0, 0, 0}; pa_lo[k] = pa_hi[k]; }
-
-    for (int ti = t0; ti < t1; ++ti) {
-        const int64_t tile = (int64_t)bg * a.tiles_per_seq + ti;
-        const uint8_t* kc = a.kc + tile * KCB;
-        const uint8_t* vc = a.vc + tile * VCB;
-
-        // ---- issue the tile's code loads (one contiguous run per lane) ----
-        uint32_t kw[TILE / 16][KW];   // 8 M-blocks of 16 tokens
+    // Loads run one tile ahead, each issued once its registers are free: the
+    // next tile's meta right after this tile's meta is in LDS, its K codes
+    // after the q.K^T products, its V codes after the p.V products.  Every
+    // load is unconditional (past the last tile the last one is re-read), so
+    // each wait covers a fixed number of younger loads.
+    constexpr int KC = 2 * L::KMH / 16, VC = 2 * L::VMH / 16;   // 16-byte meta chunks
+    constexpr int MCH = (KC + VC + 63) / 64;                      // chunks per lane
+    uint32_t kw[TILE / 16][KW];   // K codes: 8 M-blocks of 16 tokens, one run per lane
+    uint32_t vw[NKB][VW];         // V codes: D/16 N-blocks of 16 channels
+    uint4 mt[MCH];                // meta chunks
+    auto tile_index = [&](int ti) { return (int64_t)bg * a.tiles_per_seq + (ti < t1 ? ti : t1 - 1); };
+    auto load_k = [&](int ti) {
+        const uint8_t* kc = a.kc + tile_index(ti) * KCB;
 #pragma unroll
         for (int mb = 0; mb < TILE / 16; ++mb) {
             const uint8_t* p = kc + (size_t)(16 * mb + mrow) * KROW + mgrp * (KROW / 4);
@@ -290,7 +289,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 kw[mb][0] = *reinterpret_cast<const uint32_t*>(p);
             }
         }
-        uint32_t vw[NKB][VW];   // D/16 N-blocks of 16 channels
+    };
+    auto load_v = [&](int ti) {
+        const uint8_t* vc = a.vc + tile_index(ti) * VCB;
 #pragma unroll
         for (int nb = 0; nb < NKB; ++nb) {
             const uint8_t* p = vc + (size_t)(16 * nb + mrow) * VROW + mgrp * (VROW / 4);
@@ -302,16 +303,34 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 vw[nb][0] = v.x; vw[nb][1] = v.y;
             }
         }
-        // ---- meta of the tile into the wave's LDS ----
-        {
-            const uint4* km = reinterpret_cast<const uint4*>(a.km + tile * L::KMH);
-            const uint4* vm = reinterpret_cast<const uint4*>(a.vm + tile * L::VMH);
-            constexpr int KC = 2 * L::KMH / 16, VC = 2 * L::VMH / 16;
-            for (int k = lane; k < KC + VC; k += 64) {
-                if (k < KC) reinterpret_cast<uint4*>(kmeta)[k] = km[k];
-                else reinterpret_cast<uint4*>(vmeta)[k - KC] = vm[k - KC];
-            }
+    };
+    auto load_meta = [&](int ti) {
+        const int64_t tile = tile_index(ti);
+        const uint4* km = reinterpret_cast<const uint4*>(a.km + tile * L::KMH);
+        const uint4* vm = reinterpret_cast<const uint4*>(a.vm + tile * L::VMH);
+#pragma unroll
+        for (int r = 0; r < MCH; ++r) {
+            int k = lane + 64 * r;
+            if (k >= KC + VC) k = 0;   // spare lanes re-read chunk 0
+            const uint4* src = (k < KC) ? km + k : vm + (k - KC);
+            mt[r] = *src;
         }
+    };
+    load_meta(t0);
+    load_k(t0);
+    load_v(t0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile, once
+
+    for (int ti = t0; ti < t1; ++ti) {
+        // ---- meta of the tile into the wave's LDS, then the next tile's meta ----
+        // (the K and V meta images are adjacent: chunk k lands at byte 16 k)
+        static_assert(L::vmeta(0) == 16 * KC, "meta images must be adjacent");
+#pragma unroll
+        for (int r = 0; r < MCH; ++r) {
+            const uint4 v = mt[r];
+            if (lane + 64 * r < KC + VC) reinterpret_cast<uint4*>(kmeta)[lane + 64 * r] = v;
+        }
+        load_meta(ti + 1);
         wave_sync();
 
         // ---- q' = qh * SK (hi/lo, scaled), zero-point term ----
@@ -349,12 +368,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             }
         }
         wave_sync();
-        if (mrow < G) {
+        // MFMA B operand: q' rows n < G, zero rows above
+        h4_t bq_hi[NKB], bq_lo[NKB];
+        {
+            const int row = mrow < G ? mrow : G - 1;
+            const h4_t z = {0, 0, 0, 0};
 #pragma unroll
             for (int k = 0; k < NKB; ++k) {
-                const int off = ((mgrp * G + mrow) * NKB + k) * 8;
-                bq_hi[k] = *reinterpret_cast<const h4_t*>(bqimg + off);
-                bq_lo[k] = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
+                const int off = ((mgrp * G + row) * NKB + k) * 8;
+                const h4_t hi = *reinterpret_cast<const h4_t*>(bqimg + off);
+                const h4_t lo = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
+                bq_hi[k] = mrow < G ? hi : z;
+                bq_lo[k] = mrow < G ? lo : z;
             }
         }
 
@@ -371,6 +396,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             if (mrow < G)
                 *reinterpret_cast<f4_t*>(sc + mrow * TILE + 16 * mb + 4 * mgrp) = c;
         }
+        load_k(ti + 1);
         wave_sync();
 
         // ---- online softmax, dense: task t = (query t/16, lane group, pair) ----
@@ -431,12 +457,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             }
         }
         wave_sync();
-        if (mrow < G) {
+        // MFMA A operand: p' rows n < G, zero rows above
+        h4_t pa_hi[NVB], pa_lo[NVB];
+        {
+            const int row = mrow < G ? mrow : G - 1;
+            const h4_t z = {0, 0, 0, 0};
 #pragma unroll
             for (int k = 0; k < NVB; ++k) {
-                const int off = ((mgrp * G + mrow) * NVB + k) * 8;
-                pa_hi[k] = *reinterpret_cast<const h4_t*>(paimg + off);
-                pa_lo[k] = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
+                const int off = ((mgrp * G + row) * NVB + k) * 8;
+                const h4_t hi = *reinterpret_cast<const h4_t*>(paimg + off);
+                const h4_t lo = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
+                pa_hi[k] = mrow < G ? hi : z;
+                pa_lo[k] = mrow < G ? lo : z;
             }
         }
 
@@ -453,6 +485,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             if (4 * mgrp < G)
                 *reinterpret_cast<f4_t*>(pvc + (16 * nb + mrow) * GP + 4 * mgrp) = c;
         }
+        load_v(ti + 1);
         wave_sync();
 
         // ---- dense update of the accumulator ----
