@@ -232,6 +232,20 @@ __device__ __forceinline__ void rg_minmax4(float (&v)[4]) {
     }
 }
 
+// Three-way min / max of values that are results of arithmetic (never
+// signalling NaNs): written out so that no canonicalising operation is
+// inserted for operands that come from LDS.
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Flat-group test of the normalisation in fp32: a spread below 2^-16 of the
 // group mean cannot be told apart from a constant group.
 __device__ __forceinline__ bool is_flat(float sd, float mean) {

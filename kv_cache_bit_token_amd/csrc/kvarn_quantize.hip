@@ -26,8 +26,8 @@
 //  * Each std comes from the raw moments sum(v) and sum(v^2) of v = X' * f
 //    (f the cross-axis factor) in one pass; the factor's reciprocal is the
 //    hardware reciprocal square root of the variance (about 1 ulp).  Where
-//    the mean is large next to the spread (mean^2 > var/4, or var <= 0,
-//    which also catches flat groups) the moments lose accuracy to
+//    the mean is large next to the spread (4 mean^2 >= var, which includes
+//    var <= 0 and so every flat group) the moments lose accuracy to
 //    cancellation, and that pass is recomputed with the two-pass centred
 //    formula: per tile for a column pass, per token for a row pass.
 //  * A K group (one channel) is scaled by its own column factor, which
@@ -145,12 +145,13 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             s2 += dpp<DPP_XOR1>(s2);
             cmean = s1 * (1.0f / TILE);
             const float var = __builtin_fmaf(-cmean, cmean, s2 * (1.0f / TILE));
-            if ((var > 0.0f) && (cmean * cmean <= 0.25f * var)) {
-                Cinv = __builtin_amdgcn_rsqf(var);
-                Cp = var * Cinv;
-            } else {
-                *flag = 1;
-            }
+            // accurate unless the mean dominates the spread (4 mean^2 >= var,
+            // which also covers var <= 0)
+            const bool ok = 4.0f * cmean * cmean < var;
+            const float ci = __builtin_amdgcn_rsqf(var);
+            Cinv = ok ? ci : Cinv;
+            Cp = ok ? var * ci : Cp;
+            if (!ok) *flag = 1;
             if (rh == 0) colv[rp] = Cinv;
         }
         __syncthreads();
@@ -204,10 +205,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             s2 = rg_sum<R>(s2);
             const float mean = s1 * (1.0f / D);
             const float var = __builtin_fmaf(-mean, mean, s2 * (1.0f / D));
-            if ((var > 0.0f) && (mean * mean <= 0.25f * var)) {
-                a[i] = __builtin_amdgcn_rsqf(var);
-                Rt[i] = var * a[i];
-            } else {
+            float ai = __builtin_amdgcn_rsqf(var);
+            float ri = var * ai;
+            if (!(4.0f * mean * mean < var)) {
                 // fallback for this token (uniform across its row-group)
                 float q = 0.0f;
 #pragma unroll
@@ -216,9 +216,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
                     q = __builtin_fmaf(d, d, q);
                 }
                 const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
-                if (!is_flat(sd, mean)) Rt[i] = sd;
-                a[i] = 1.0f / Rt[i];
+                ri = is_flat(sd, mean) ? Rt[i] : sd;
+                ai = 1.0f / ri;
             }
+            a[i] = ai;
+            Rt[i] = ri;
         }
     }
 
@@ -261,15 +263,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         }
         __syncthreads();
         {
-            float mn = rpart[0].x, mx = rpart[0].y;
+            float2 v[16];
 #pragma unroll
-            for (int k = 1; k < 16; ++k) {
-                const float2 v = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
-                mn = fminf(mn, v.x);
-                mx = fmaxf(mx, v.y);
+            for (int k = 0; k < 16; ++k) v[k] = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
+            float mn = min3f(v[0].x, v[1].x, v[2].x), mx = max3f(v[0].y, v[1].y, v[2].y);
+#pragma unroll
+            for (int k = 3; k < 15; k += 2) {
+                mn = min3f(mn, v[k].x, v[k + 1].x);
+                mx = max3f(mx, v[k].y, v[k + 1].y);
             }
-            mn = fminf(mn, dpp<DPP_XOR1>(mn));
-            mx = fmaxf(mx, dpp<DPP_XOR1>(mx));
+            mn = min3f(mn, v[15].x, dpp<DPP_XOR1>(min3f(mn, v[15].x, v[15].x)));
+            mx = max3f(mx, v[15].y, dpp<DPP_XOR1>(max3f(mx, v[15].y, v[15].y)));
             const float zk = mn;
             const float range = mx - mn;
             const float sk = range * (1.0f / (float)L);
