@@ -23,6 +23,7 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
+_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def _load():
@@ -54,6 +55,9 @@ def _load():
         "oracle_dequantize_tiles": (None, [_i64, _int, _int, _int, _u8p, _u16p, _dp, _u16p]),
         "oracle_decode_attention": (None, [_int, _int, _int, _int, _int, _int, _int, _u16p,
                                            _u8p, _u8p, _u16p, _u16p, ctypes.c_double, _dp]),
+        "oracle_decode_attention_paged": (None, [_int, _int, _int, _int, _int, _int, _int, _i32p,
+                                                 _i32p, _i32p, _u16p, _u8p, _u8p, _u16p, _u16p,
+                                                 _u16p, _u16p, ctypes.c_double, _dp]),
         "oracle_set_threads": (None, [_int]),
         "oracle_max_threads": (_int, []),
     }
@@ -241,4 +245,32 @@ def decode_attention(q16, k_codes, v_codes, k_meta16, v_meta16, *, n_kv_heads: i
                                     int(k_bits), int(v_bits), _ptr(q, _u16p),
                                     _ptr(kc, _u8p), _ptr(vc, _u8p), _ptr(km, _u16p),
                                     _ptr(vm, _u16p), float(sm_scale), _ptr(out, _dp))
+    return out
+
+
+def decode_attention_paged(q16, k_codes, v_codes, k_meta16, v_meta16, block_table, n_blocks,
+                           tail_len, k_tail16, v_tail16, *, n_kv_heads: int, k_bits: int = 4,
+                           v_bits: int = 2, sm_scale: float = None):
+    """Paged cache plus fp16 tail.  block_table [batch][max_blocks] int32 (physical
+    block p holds tiles p * n_kv_heads + g), n_blocks / tail_len [batch] int32,
+    k_tail / v_tail [batch][n_kv_heads][128][d0] float16.  -> [batch][hq][d0] f64."""
+    q = _h(q16)
+    batch, hq, d0 = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d0)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    nb = np.ascontiguousarray(n_blocks, dtype=np.int32)
+    tl = np.ascontiguousarray(tail_len, dtype=np.int32)
+    assert bt.ndim == 2 and bt.shape[0] == batch and nb.shape == (batch,) and tl.shape == (batch,)
+    kc = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    vc = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    km, vm = _h(k_meta16), _h(v_meta16)
+    kt, vt = _h(k_tail16), _h(v_tail16)
+    assert kt.shape == (batch, n_kv_heads, 128, d0) and vt.shape == kt.shape
+    out = np.empty((batch, hq, d0), np.float64)
+    _load().oracle_decode_attention_paged(
+        batch, hq, int(n_kv_heads), bt.shape[1], d0, int(k_bits), int(v_bits),
+        bt.ctypes.data_as(_i32p), nb.ctypes.data_as(_i32p), tl.ctypes.data_as(_i32p),
+        _ptr(q, _u16p), _ptr(kc, _u8p), _ptr(vc, _u8p), _ptr(km, _u16p), _ptr(vm, _u16p),
+        _ptr(kt, _u16p), _ptr(vt, _u16p), float(sm_scale), _ptr(out, _dp))
     return out

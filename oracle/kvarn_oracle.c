@@ -483,10 +483,50 @@ void oracle_dequantize_tiles(int64_t n_tiles, int d0, int bits, int is_key,
 /* Decode attention over the quantised cache: the textbook formula applied   */
 /* to the dequantised (double, not rounded) K and V.  Query head h reads KV  */
 /* head h / (n_q_heads / n_kv_heads).  s_t = sm_scale * q . k_t;             */
-/* p = softmax(s) (max subtracted); o = sum_t p_t v_t.                       */
+/* p = softmax(s) (max subtracted); o = sum_t p_t v_t.  An empty sequence    */
+/* (no tokens) gives o = 0.                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* One (sequence, KV head): the group's query heads over T tokens of K, V    */
+/* ([T][d0] double).  q: the sequence's [n_q_heads][d0] binary16 queries.    */
+static void oracle_attend_group(const uint16_t *q, int g, int group, int64_t T, int d0,
+                                const double *K, const double *V, double sm_scale,
+                                double *sc, double *out)
+{
+    for (int hh = 0; hh < group; ++hh) {
+        int h = g * group + hh;
+        const uint16_t *qh = q + (size_t)h * d0;
+        double *o = out + (size_t)h * d0;
+        for (int j = 0; j < d0; ++j)
+            o[j] = 0.0;
+        if (T == 0)
+            continue;
+        double qd[256];
+        for (int j = 0; j < d0; ++j)
+            qd[j] = oracle_half_to_double(qh[j]);
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int j = 0; j < d0; ++j)
+                acc += qd[j] * K[(size_t)t * d0 + j];
+            sc[t] = sm_scale * acc;
+            if (sc[t] > mx) mx = sc[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            sc[t] = exp(sc[t] - mx);
+            l += sc[t];
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            double p = sc[t] / l;
+            for (int j = 0; j < d0; ++j)
+                o[j] += p * V[(size_t)t * d0 + j];
+        }
+    }
+}
+
 /* Cache tile i of (b, g) is at index (b * n_kv_heads + g) * tiles_per_seq + i.
  * q: [batch][n_q_heads][d0] binary16; out: [batch][n_q_heads][d0] double.   */
-/* ------------------------------------------------------------------------ */
 void oracle_decode_attention(int batch, int n_q_heads, int n_kv_heads, int tiles_per_seq,
                              int d0, int k_bits, int v_bits, const uint16_t *q,
                              const uint8_t *k_codes, const uint8_t *v_codes,
@@ -501,9 +541,9 @@ void oracle_decode_attention(int batch, int n_q_heads, int n_kv_heads, int tiles
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t bg = 0; bg < (int64_t)batch * n_kv_heads; ++bg) {
         int b = (int)(bg / n_kv_heads), g = (int)(bg % n_kv_heads);
-        double *K = malloc((size_t)T * d0 * sizeof(double));
-        double *V = malloc((size_t)T * d0 * sizeof(double));
-        double *sc = malloc((size_t)T * sizeof(double));
+        double *K = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *V = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *sc = malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
         for (int i = 0; i < tiles_per_seq; ++i) {
             int64_t tile = bg * tiles_per_seq + i;
             oracle_dequantize_tile(k_codes + tile * kcb, k_meta + tile * kmh, d0, k_bits, 1,
@@ -511,34 +551,61 @@ void oracle_decode_attention(int batch, int n_q_heads, int n_kv_heads, int tiles
             oracle_dequantize_tile(v_codes + tile * vcb, v_meta + tile * vmh, d0, v_bits, 0,
                                    V + (size_t)i * TILE * d0);
         }
-        for (int hh = 0; hh < group; ++hh) {
-            int h = g * group + hh;
-            const uint16_t *qh = q + ((size_t)b * n_q_heads + h) * d0;
-            double qd[256];
-            for (int j = 0; j < d0; ++j)
-                qd[j] = oracle_half_to_double(qh[j]);
-            double mx = -INFINITY;
-            for (int64_t t = 0; t < T; ++t) {
-                double acc = 0.0;
-                for (int j = 0; j < d0; ++j)
-                    acc += qd[j] * K[(size_t)t * d0 + j];
-                sc[t] = sm_scale * acc;
-                if (sc[t] > mx) mx = sc[t];
-            }
-            double l = 0.0;
-            for (int64_t t = 0; t < T; ++t) {
-                sc[t] = exp(sc[t] - mx);
-                l += sc[t];
-            }
-            double *o = out + ((size_t)b * n_q_heads + h) * d0;
-            for (int j = 0; j < d0; ++j)
-                o[j] = 0.0;
-            for (int64_t t = 0; t < T; ++t) {
-                double p = sc[t] / l;
-                for (int j = 0; j < d0; ++j)
-                    o[j] += p * V[(size_t)t * d0 + j];
-            }
+        oracle_attend_group(q + (size_t)b * n_q_heads * d0, g, group, T, d0, K, V, sm_scale, sc,
+                            out + (size_t)b * n_q_heads * d0);
+        free(K);
+        free(V);
+        free(sc);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over a paged cache with an fp16 tail (deep page, section */
+/* on running inside vLLM's PagedAttention: one 128-token page is one        */
+/* quantisation tile, its scales travel with the page; the tokens of a       */
+/* sequence that do not fill a page yet stay in a separate decode            */
+/* workspace).  Sequence b's logical block i is the physical block           */
+/* p = block_table[b * max_blocks + i], i < n_blocks[b]; physical block p    */
+/* holds the tiles p * n_kv_heads + g.  Its tokens are those of its blocks   */
+/* in order, then the first tail_len[b] rows of the binary16 tail            */
+/* k_tail/v_tail [batch][n_kv_heads][128][d0], taken as they are.            */
+/* ------------------------------------------------------------------------ */
+void oracle_decode_attention_paged(int batch, int n_q_heads, int n_kv_heads, int max_blocks,
+                                   int d0, int k_bits, int v_bits, const int32_t *block_table,
+                                   const int32_t *n_blocks, const int32_t *tail_len,
+                                   const uint16_t *q, const uint8_t *k_codes,
+                                   const uint8_t *v_codes, const uint16_t *k_meta,
+                                   const uint16_t *v_meta, const uint16_t *k_tail,
+                                   const uint16_t *v_tail, double sm_scale, double *out)
+{
+    int D = oracle_padded_dim(d0);
+    int group = n_q_heads / n_kv_heads;
+    int64_t kcb = oracle_code_bytes(D, k_bits), vcb = oracle_code_bytes(D, v_bits);
+    int64_t kmh = oracle_meta_halves(D, 1), vmh = oracle_meta_halves(D, 0);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)batch * n_kv_heads; ++bg) {
+        int b = (int)(bg / n_kv_heads), g = (int)(bg % n_kv_heads);
+        int nb = n_blocks[b], tl = tail_len[b];
+        int64_t T = (int64_t)nb * TILE + tl;
+        double *K = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *V = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *sc = malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+        for (int i = 0; i < nb; ++i) {
+            int64_t tile = (int64_t)block_table[(size_t)b * max_blocks + i] * n_kv_heads + g;
+            oracle_dequantize_tile(k_codes + tile * kcb, k_meta + tile * kmh, d0, k_bits, 1,
+                                   K + (size_t)i * TILE * d0);
+            oracle_dequantize_tile(v_codes + tile * vcb, v_meta + tile * vmh, d0, v_bits, 0,
+                                   V + (size_t)i * TILE * d0);
         }
+        const uint16_t *kt = k_tail + ((size_t)b * n_kv_heads + g) * TILE * d0;
+        const uint16_t *vt = v_tail + ((size_t)b * n_kv_heads + g) * TILE * d0;
+        for (int t = 0; t < tl; ++t)
+            for (int j = 0; j < d0; ++j) {
+                K[((size_t)nb * TILE + t) * d0 + j] = oracle_half_to_double(kt[(size_t)t * d0 + j]);
+                V[((size_t)nb * TILE + t) * d0 + j] = oracle_half_to_double(vt[(size_t)t * d0 + j]);
+            }
+        oracle_attend_group(q + (size_t)b * n_q_heads * d0, g, group, T, d0, K, V, sm_scale, sc,
+                            out + (size_t)b * n_q_heads * d0);
         free(K);
         free(V);
         free(sc);

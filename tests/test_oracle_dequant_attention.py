@@ -131,3 +131,74 @@ def test_kvarn_beats_naive_rtn_on_outlier_data():
                                 n_kv_heads=n_kv, tiles_per_seq=T // 128)
     naive = _sdpa_ref(q, _naive_rtn(k, 4), _naive_rtn(v, 2), n_kv)
     assert rel(o, ref) < rel(naive, ref)
+
+
+# ---- paged cache with an fp16 tail (deep page, running inside vLLM's
+# PagedAttention: a 128-token page is one tile, scales travel with it; the
+# unfilled page stays in a separate decode workspace) ----
+
+def _paged_case(seed, B=4, n_kv=2, Hq=8, max_blocks=3, d0=128):
+    from kv_cache_bit_token_amd.paged import paged_layout
+    table, nb, tl, pool = paged_layout(seed, B, max_blocks)
+    k, v = synthetic.outlier_kv_host(seed, pool * n_kv, 128, d0)
+    kq, vq = _quantize_pair(synthetic.as_tiles(k), synthetic.as_tiles(v))
+    kt, vt = synthetic.outlier_kv_host(seed + 1, B * n_kv, 128, d0)
+    kt, vt = kt.reshape(B, n_kv, 128, d0), vt.reshape(B, n_kv, 128, d0)
+    q = synthetic.query_host(seed, B, Hq, d0)
+    return table, nb, tl, kq, vq, kt, vt, q
+
+
+def test_paged_attention_is_sdpa_over_blocks_then_tail():
+    d0, n_kv, Hq = 128, 2, 8
+    table, nb, tl, kq, vq, kt, vt, q = _paged_case(31)
+    o = oracle.decode_attention_paged(q, kq["codes"], vq["codes"], kq["meta"], vq["meta"], table,
+                                      nb, tl, kt, vt, n_kv_heads=n_kv)
+    Kd, _ = oracle.dequantize_tiles(kq["codes"], kq["meta"], d0, 4, True)
+    Vd, _ = oracle.dequantize_tiles(vq["codes"], vq["meta"], d0, 2, False)
+    for b in range(table.shape[0]):
+        T = nb[b] * 128 + tl[b]
+        if T == 0:
+            assert np.all(o[b] == 0.0)
+            continue
+        Ks, Vs = [], []
+        for g in range(n_kv):
+            tiles = table[b, :nb[b]].astype(np.int64) * n_kv + g
+            Ks.append(np.concatenate([Kd[tiles].reshape(-1, d0), kt[b, g, :tl[b]].astype(np.float64)]))
+            Vs.append(np.concatenate([Vd[tiles].reshape(-1, d0), vt[b, g, :tl[b]].astype(np.float64)]))
+        ref = _sdpa_ref(q[b:b + 1], np.stack(Ks), np.stack(Vs), n_kv)
+        assert np.allclose(o[b:b + 1], ref, rtol=0, atol=1e-12), b
+
+
+def test_paged_attention_tail_only_is_fp16_attention():
+    d0, n_kv, Hq, B = 96, 1, 4, 2
+    kt, vt = synthetic.outlier_kv_host(7, B * n_kv, 128, d0)
+    kt, vt = kt.reshape(B, n_kv, 128, d0), vt.reshape(B, n_kv, 128, d0)
+    q = synthetic.query_host(7, B, Hq, d0)
+    tl = np.array([128, 5], np.int32)
+    empty = np.zeros((0,), np.uint8)
+    o = oracle.decode_attention_paged(q, empty, empty, np.zeros((0,), np.float16),
+                                      np.zeros((0,), np.float16), np.zeros((B, 1), np.int32),
+                                      np.zeros(B, np.int32), tl, kt, vt, n_kv_heads=n_kv)
+    for b in range(B):
+        ref = _sdpa_ref(q[b:b + 1], kt[b, :, :tl[b]].astype(np.float64),
+                        vt[b, :, :tl[b]].astype(np.float64), n_kv)
+        assert np.allclose(o[b:b + 1], ref, rtol=0, atol=1e-12)
+
+
+def test_paged_attention_ignores_pool_placement():
+    """Moving the blocks to other pool slots (and the table with them)
+    changes nothing: the scales travel with their block."""
+    n_kv = 2
+    table, nb, tl, kq, vq, kt, vt, q = _paged_case(41)
+    o1 = oracle.decode_attention_paged(q, kq["codes"], vq["codes"], kq["meta"], vq["meta"], table,
+                                       nb, tl, kt, vt, n_kv_heads=n_kv)
+    pool = kq["codes"].shape[0] // n_kv
+    perm = np.random.default_rng(0).permutation(pool)     # new slot of block p
+    inv = np.argsort(perm)
+    idx = (inv[:, None] * n_kv + np.arange(n_kv)[None, :]).reshape(-1)
+    moved = {key: arr[idx] for key, arr in (("kc", kq["codes"]), ("vc", vq["codes"]),
+                                             ("km", kq["meta"]), ("vm", vq["meta"]))}
+    table2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1).astype(np.int32)
+    o2 = oracle.decode_attention_paged(q, moved["kc"], moved["vc"], moved["km"], moved["vm"],
+                                       table2, nb, tl, kt, vt, n_kv_heads=n_kv)
+    assert np.array_equal(o1, o2)
