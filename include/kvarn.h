@@ -132,6 +132,54 @@ kvarn_status kvarn_decode_attention(const kvarn_params *params, int32_t batch,
                                     float sm_scale, float *out, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/* ---- paged cache (deep page, the section on running inside vLLM's
+ * PagedAttention: one 128-token page is one tile and its scales travel with
+ * the page; the tokens that do not fill a page yet stay apart, in fp16, in a
+ * decode workspace) ---- */
+
+/* kvarn_quantize_tiles into chosen slots of a tile pool: input tile i of K and
+ * of V is written to pool tile dst_tile[i] of the codes and meta arrays.
+ *   dst_tile  [n_tiles] int64, device, read only; entries outside
+ *             [0, pool_tiles) skip that input tile (nothing is written)
+ *   k_codes.. [pool_tiles][...] as in kvarn_quantize_tiles
+ * Two entries naming the same slot leave that slot unspecified. */
+kvarn_status kvarn_quantize_tiles_to(const kvarn_params *params, int64_t n_tiles,
+                                     const void *k_fp16, const void *v_fp16,
+                                     const int64_t *dst_tile, int64_t pool_tiles,
+                                     void *k_codes, void *v_codes,
+                                     void *k_meta, void *v_meta, void *stream);
+
+/* Workspace (bytes) that kvarn_decode_attention_paged needs for this shape. */
+kvarn_status kvarn_decode_attention_paged_workspace(const kvarn_params *params, int32_t batch,
+                                                    int32_t n_q_heads, int32_t n_kv_heads,
+                                                    int32_t max_blocks, size_t *bytes);
+
+/* One decode step of GQA attention over a paged packed cache plus an fp16 tail.
+ * Sequence b's tokens are those of its n_blocks[b] blocks, in table order,
+ * then the first tail_len[b] rows of its tail.
+ *   block_table [batch][max_blocks] int32, device: physical block of logical
+ *               block i of sequence b; physical block p holds the tiles
+ *               p * n_kv_heads + g (g = KV head) of the pool arrays
+ *   n_blocks    [batch] int32, device: used blocks, read as clamped to
+ *               0..max_blocks
+ *   tail_len    [batch] int32, device: 0..128 tail tokens (clamped)
+ *   k_tail, v_tail [batch][n_kv_heads][128][head_dim] fp16, device
+ *   pool arrays k_codes .. v_meta hold pool_blocks * n_kv_heads tiles
+ *   q, out, sm_scale as in kvarn_decode_attention; a sequence with no tokens
+ *   gets out = 0.
+ * Table entries outside [0, pool_blocks) are read as block 0 (no access
+ * outside the pool; that sequence's output is then unspecified). */
+kvarn_status kvarn_decode_attention_paged(const kvarn_params *params, int32_t batch,
+                                          int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t max_blocks, int64_t pool_blocks,
+                                          const int32_t *block_table, const int32_t *n_blocks,
+                                          const int32_t *tail_len, const void *q_fp16,
+                                          const void *k_codes, const void *v_codes,
+                                          const void *k_meta, const void *v_meta,
+                                          const void *k_tail, const void *v_tail,
+                                          float sm_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *kvarn_status_str(kvarn_status status);
 

@@ -172,3 +172,92 @@ def decode_attention(q, k_codes, v_codes, k_meta, v_meta, *, n_kv_heads, tiles_p
                                     workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("kvarn_decode_attention", st)
     return out
+
+
+def quantize_tiles_to(k, v, dst_tile, k_codes, v_codes, k_meta, v_meta, *, k_bits=4, v_bits=2,
+                      n_iters=5):
+    """Quantise fp16 K and V tiles into chosen slots of a tile pool.
+
+    k, v: torch.float16 GPU tensors [..., 128, head_dim] (either may be None);
+    dst_tile: torch.int64 GPU tensor [n_tiles], the pool slot of each input
+    tile (slots outside the pool skip their tile); k_codes .. v_meta: the pool
+    tensors, [pool_tiles, ...] as returned by quantize_tiles, written in place.
+    """
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("nothing to quantise")
+    head_dim = ref.shape[-1]
+    n_tiles = ref.numel() // (TILE * head_dim)
+    for t, name in ((k, "k"), (v, "v")):
+        _need_gpu(t, name, torch.float16)
+        if t is not None and (t.shape[-2] != TILE or t.numel() != n_tiles * TILE * head_dim):
+            raise ValueError("%s must be [..., 128, head_dim] with the same tile count" % name)
+    _need_gpu(dst_tile, "dst_tile", torch.int64)
+    if dst_tile.numel() != n_tiles:
+        raise ValueError("dst_tile needs one entry per input tile")
+    pool = (k_codes if k is not None else v_codes).shape[0]
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, n_iters)
+    st = lib.kvarn_quantize_tiles_to(ctypes.byref(p), n_tiles, _ptr(k), _ptr(v), _ptr(dst_tile),
+                                     int(pool), _ptr(k_codes if k is not None else None),
+                                     _ptr(v_codes if v is not None else None),
+                                     _ptr(k_meta if k is not None else None),
+                                     _ptr(v_meta if v is not None else None), _stream(ref.device))
+    _check("kvarn_quantize_tiles_to", st)
+
+
+def decode_attention_paged_workspace(*, batch, n_q_heads, n_kv_heads, max_blocks, head_dim,
+                                     k_bits=4, v_bits=2):
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    nb = ctypes.c_size_t()
+    _check("kvarn_decode_attention_paged_workspace",
+           lib.kvarn_decode_attention_paged_workspace(ctypes.byref(p), int(batch), int(n_q_heads),
+                                                      int(n_kv_heads), int(max_blocks),
+                                                      ctypes.byref(nb)))
+    return nb.value
+
+
+def decode_attention_paged(q, k_codes, v_codes, k_meta, v_meta, block_table, n_blocks, tail_len,
+                           k_tail, v_tail, *, n_kv_heads, k_bits=4, v_bits=2, sm_scale=None,
+                           workspace=None, out=None):
+    """One decode step over a paged packed cache plus an fp16 tail.
+
+    q: float16 [batch, n_q_heads, head_dim]; block_table: int32
+    [batch, max_blocks] (physical block p holds pool tiles p * n_kv_heads + g);
+    n_blocks, tail_len: int32 [batch]; k_tail, v_tail: float16
+    [batch, n_kv_heads, 128, head_dim]; pool tensors as from quantize_tiles
+    with pool_blocks * n_kv_heads rows.  Returns float32 [batch, n_q_heads, head_dim].
+    """
+    _need_gpu(q, "q", torch.float16)
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need_gpu(t, name, torch.uint8)
+    for t, name in ((k_meta, "k_meta"), (v_meta, "v_meta"), (k_tail, "k_tail"), (v_tail, "v_tail")):
+        _need_gpu(t, name, torch.float16)
+    for t, name in ((block_table, "block_table"), (n_blocks, "n_blocks"), (tail_len, "tail_len")):
+        _need_gpu(t, name, torch.int32)
+    batch, hq, head_dim = q.shape
+    max_blocks = block_table.shape[1]
+    if block_table.shape[0] != batch or n_blocks.numel() != batch or tail_len.numel() != batch:
+        raise ValueError("block_table, n_blocks and tail_len need one row per sequence")
+    if tuple(k_tail.shape) != (batch, n_kv_heads, TILE, head_dim) or k_tail.shape != v_tail.shape:
+        raise ValueError("k_tail, v_tail must be [batch, n_kv_heads, 128, head_dim]")
+    pool_blocks = k_codes.shape[0] // n_kv_heads
+    if sm_scale is None:
+        sm_scale = head_dim ** -0.5
+    nbytes = decode_attention_paged_workspace(batch=batch, n_q_heads=hq, n_kv_heads=n_kv_heads,
+                                              max_blocks=max_blocks, head_dim=head_dim,
+                                              k_bits=k_bits, v_bits=v_bits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, hq, head_dim), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    st = lib.kvarn_decode_attention_paged(
+        ctypes.byref(p), batch, hq, int(n_kv_heads), int(max_blocks), int(pool_blocks),
+        _ptr(block_table), _ptr(n_blocks), _ptr(tail_len), _ptr(q), _ptr(k_codes), _ptr(v_codes),
+        _ptr(k_meta), _ptr(v_meta), _ptr(k_tail), _ptr(v_tail), float(sm_scale), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("kvarn_decode_attention_paged", st)
+    return out

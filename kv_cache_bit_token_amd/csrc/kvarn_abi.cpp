@@ -224,8 +224,123 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, int32_t batch, i
     a.tiles_per_seq = tiles_per_seq;
     a.n_splits = ns;
     a.tiles_per_split = tps;
+    a.n_parts = ns;
     a.d0 = params->head_dim;
     a.sm_scale = sm_scale;
+    hipError_t e = kvarn::launch_attention(a, D, params->k_bits, params->v_bits,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVARN_OK : KVARN_E_HIP;
+}
+
+kvarn_status kvarn_quantize_tiles_to(const kvarn_params* params, int64_t n_tiles,
+                                     const void* k_fp16, const void* v_fp16,
+                                     const int64_t* dst_tile, int64_t pool_tiles, void* k_codes,
+                                     void* v_codes, void* k_meta, void* v_meta, void* stream) {
+    int D = 0;
+    kvarn_status st = check_params(params, &D);
+    if (st != KVARN_OK) return st;
+    const int ks = pointer_set(k_fp16, k_codes, k_meta);
+    const int vs = pointer_set(v_fp16, v_codes, v_meta);
+    if (ks < 0 || vs < 0) return KVARN_E_NULL;
+    if (n_tiles < 0 || n_tiles > kMaxTiles || pool_tiles < 0 || pool_tiles > kMaxTiles)
+        return KVARN_E_SHAPE;
+    if (n_tiles > 0 && (ks || vs) && !dst_tile) return KVARN_E_NULL;
+    if (misaligned(k_fp16) || misaligned(v_fp16) || misaligned(k_codes) || misaligned(v_codes) ||
+        misaligned(k_meta) || misaligned(v_meta) || misaligned(dst_tile))
+        return KVARN_E_ALIGN;
+    if (n_tiles == 0 || pool_tiles == 0 || (ks == 0 && vs == 0)) return KVARN_OK;
+
+    kvarn::QuantArgs a;
+    a.k = static_cast<const uint16_t*>(k_fp16);
+    a.v = static_cast<const uint16_t*>(v_fp16);
+    a.kc = static_cast<uint8_t*>(k_codes);
+    a.vc = static_cast<uint8_t*>(v_codes);
+    a.km = static_cast<uint16_t*>(k_meta);
+    a.vm = static_cast<uint16_t*>(v_meta);
+    a.n_k = ks ? n_tiles : 0;
+    a.n_v = vs ? n_tiles : 0;
+    a.d0 = params->head_dim;
+    a.n_iters = params->n_iters;
+    a.dst = dst_tile;
+    a.pool = pool_tiles;
+    hipError_t e = kvarn::launch_quantize(a, D, params->k_bits, params->v_bits,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVARN_OK : KVARN_E_HIP;
+}
+
+kvarn_status kvarn_decode_attention_paged_workspace(const kvarn_params* params, int32_t batch,
+                                                    int32_t n_q_heads, int32_t n_kv_heads,
+                                                    int32_t max_blocks, size_t* bytes) {
+    if (!bytes) return KVARN_E_NULL;
+    int D = 0;
+    kvarn_status st = check_params(params, &D);
+    if (st != KVARN_OK) return st;
+    st = check_attention_shape(batch, n_q_heads, n_kv_heads, max_blocks);
+    if (st != KVARN_OK) return st;
+    int ns = 0, tps = 0;
+    kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
+    if (max_blocks == 0) ns = 0;
+    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
+    return KVARN_OK;
+}
+
+kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t batch,
+                                          int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t max_blocks, int64_t pool_blocks,
+                                          const int32_t* block_table, const int32_t* n_blocks,
+                                          const int32_t* tail_len, const void* q_fp16,
+                                          const void* k_codes, const void* v_codes,
+                                          const void* k_meta, const void* v_meta,
+                                          const void* k_tail, const void* v_tail,
+                                          float sm_scale, float* out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    int D = 0;
+    kvarn_status st = check_params(params, &D);
+    if (st != KVARN_OK) return st;
+    st = check_attention_shape(batch, n_q_heads, n_kv_heads, max_blocks);
+    if (st != KVARN_OK) return st;
+    if (pool_blocks < 0 || pool_blocks * (int64_t)n_kv_heads > kMaxTiles) return KVARN_E_SHAPE;
+    if (!q_fp16 || !out || !workspace || !n_blocks || !tail_len || !k_tail || !v_tail)
+        return KVARN_E_NULL;
+    const bool packed = max_blocks > 0 && pool_blocks > 0;
+    if (packed && (!block_table || !k_codes || !v_codes || !k_meta || !v_meta))
+        return KVARN_E_NULL;
+    if (misaligned(q_fp16) || misaligned(out) || misaligned(workspace) || misaligned(n_blocks) ||
+        misaligned(tail_len) || misaligned(k_tail) || misaligned(v_tail) ||
+        misaligned(block_table) || misaligned(k_codes) || misaligned(v_codes) ||
+        misaligned(k_meta) || misaligned(v_meta))
+        return KVARN_E_ALIGN;
+    int ns = 0, tps = 0;
+    kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
+    if (max_blocks == 0) ns = 0;
+    if (workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
+        return KVARN_E_WORKSPACE;
+    if (batch == 0) return KVARN_OK;
+
+    kvarn::AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q_fp16);
+    a.kc = static_cast<const uint8_t*>(k_codes);
+    a.vc = static_cast<const uint8_t*>(v_codes);
+    a.km = static_cast<const uint16_t*>(k_meta);
+    a.vm = static_cast<const uint16_t*>(v_meta);
+    a.out = out;
+    a.ws = static_cast<float*>(workspace);
+    a.batch = batch;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.tiles_per_seq = max_blocks;
+    // without a pool no packed tile is read: only the tail's partial slot
+    a.n_splits = packed ? ns : 0;
+    a.tiles_per_split = tps;
+    a.n_parts = (packed ? ns : 0) + 1;
+    a.d0 = params->head_dim;
+    a.sm_scale = sm_scale;
+    a.table = block_table;
+    a.nblk = n_blocks;
+    a.tail_len = tail_len;
+    a.k_tail = static_cast<const uint16_t*>(k_tail);
+    a.v_tail = static_cast<const uint16_t*>(v_tail);
+    a.pool_blocks = pool_blocks;
     hipError_t e = kvarn::launch_attention(a, D, params->k_bits, params->v_bits,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVARN_OK : KVARN_E_HIP;

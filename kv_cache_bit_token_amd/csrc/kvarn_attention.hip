@@ -63,8 +63,8 @@ void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
     *tiles_per_split = tps;
 }
 
-size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_splits) {
-    return (size_t)batch * n_q_heads * n_splits * (D + 2) * sizeof(float);
+size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
+    return (size_t)batch * n_q_heads * n_parts * (D + 2) * sizeof(float);
 }
 
 // ---- b-bit codes -> exact fp16 (code - 2^(b-1)) -----------------------------
@@ -191,8 +191,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int split = (blockIdx.x % sgroups) * wpb + wave;
     if (split >= a.n_splits) return;
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    // tiles of this (b, g): all tiles_per_seq, or the sequence's used blocks
+    int ntiles = a.tiles_per_seq;
+    if (a.table) ntiles = min(max(a.nblk[b], 0), a.tiles_per_seq);
     const int t0 = split * a.tiles_per_split;
-    const int t1 = min(t0 + a.tiles_per_split, a.tiles_per_seq);
+    const int t1 = min(t0 + a.tiles_per_split, ntiles);
+    if (t0 >= t1) {
+        // nothing in this split: an empty partial (m = -inf, l = 0, acc = 0)
+        for (int k = lane; k < G * (D + 2); k += 64) {
+            const int n = k / (D + 2), e = k % (D + 2);
+            float* p = a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
+            p[e] = (e == 0) ? -INFINITY : 0.0f;
+        }
+        return;
+    }
 
     uint8_t* lds = smem + (size_t)wave * L::bytes(G);
     uint16_t* kmeta = reinterpret_cast<uint16_t*>(lds + L::kmeta(G));
@@ -270,7 +282,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     uint32_t kw[TILE / 16][KW];   // K codes: 8 M-blocks of 16 tokens, one run per lane
     uint32_t vw[NKB][VW];         // V codes: D/16 N-blocks of 16 channels
     uint4 mt[MCH];                // meta chunks
-    auto tile_index = [&](int ti) { return (int64_t)bg * a.tiles_per_seq + (ti < t1 ? ti : t1 - 1); };
+    // pool index of tile ti of this (b, g) (past the split's end: its last
+    // tile; a paged table entry outside the pool reads block 0)
+    auto tile_index = [&](int ti) -> int64_t {
+        const int tc = ti < t1 ? ti : t1 - 1;
+        if (!a.table) return (int64_t)bg * a.tiles_per_seq + tc;
+        int64_t blk = a.table[(size_t)b * a.tiles_per_seq + tc];
+        if (blk < 0 || blk >= a.pool_blocks) blk = 0;
+        return blk * a.n_kv_heads + g;
+    };
     auto load_k = [&](int ti) {
         const uint8_t* kc = a.kc + tile_index(ti) * KCB;
 #pragma unroll
@@ -515,7 +535,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         for (int n = 0; n < GMAX; ++n) {
             if (n < G) {
                 const int h = g * G + n;
-                float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_splits + split) * (D + 2);
+                float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_parts + split) * (D + 2);
                 p[2 + ch] = acc[r][n];
             }
         }
@@ -526,7 +546,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         const int n = t / 16;
         if (n < G && (t % 16) == 0) {
             const int h = g * G + n;
-            float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_splits + split) * (D + 2);
+            float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_parts + split) * (D + 2);
             p[0] = m_run[r];
             p[1] = l_run[r];
         }
@@ -556,17 +576,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     __shared__ float o[D];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;   // b * n_q_heads + h
-    const float* p = a.ws + (size_t)bh * a.n_splits * (D + 2);
+    const float* p = a.ws + (size_t)bh * a.n_parts * (D + 2);
     float M = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, p[s * (D + 2)]);
+    for (int s = 0; s < a.n_parts; ++s) M = fmaxf(M, p[s * (D + 2)]);
     float L = 0.0f;
-    for (int s = 0; s < a.n_splits; ++s) {
+    for (int s = 0; s < a.n_parts; ++s) {
         const float ms = p[s * (D + 2)];
         if (ms != -INFINITY) L += p[s * (D + 2) + 1] * exp2f((ms - M) * kLog2e);
     }
     for (int j = tid; j < D; j += blockDim.x) {
         float v = 0.0f;
-        for (int s = 0; s < a.n_splits; ++s) {
+        for (int s = 0; s < a.n_parts; ++s) {
             const float ms = p[s * (D + 2)];
             if (ms != -INFINITY) v += p[s * (D + 2) + 2 + j] * exp2f((ms - M) * kLog2e);
         }
@@ -577,6 +597,126 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int j = tid; j < a.d0; j += blockDim.x) a.out[(size_t)bh * a.d0 + j] = o[j];
 }
 
+// ---- fp16 tail of a paged sequence (at most 128 tokens, not yet a tile) ----
+// One 64-lane workgroup per (b, KV head): plain fp32 attention of the group's
+// query heads over the tail's fp16 K and V, in the original channel domain
+// (the scores are the same in either domain, the rotation being orthonormal).
+// Its partial (m, l, acc) goes to the last slot of the workspace with acc
+// rotated (H acc / sqrt(D)), so that the combine kernel's final rotation
+// returns it to the original domain together with the packed tiles' slots.
+template <int D>
+__global__ __launch_bounds__(64) void attn_tail_kernel(AttnArgs a) {
+    constexpr int GM = 16;
+    __shared__ float qs[GM * D];
+    __shared__ float ps[TILE * GM];
+    __shared__ float os[GM * D];
+    const int lane = threadIdx.x;
+    const int bg = blockIdx.x;
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const int d0 = a.d0;
+    const int T = min(max(a.tail_len[b], 0), TILE);
+    const int slot = a.n_parts - 1;
+    auto part = [&](int n) {
+        return a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + slot) * (D + 2);
+    };
+    if (T == 0) {
+        for (int k = lane; k < G * (D + 2); k += 64) part(k / (D + 2))[k % (D + 2)] = (k % (D + 2) == 0) ? -INFINITY : 0.0f;
+        return;
+    }
+    for (int k = lane; k < G * D; k += 64) {
+        const int n = k / D, j = k % D;
+        qs[k] = (j < d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + g * G + n) * d0 + j]) : 0.0f;
+    }
+    __syncthreads();
+    const uint16_t* kt = a.k_tail + (size_t)bg * TILE * d0;
+    const uint16_t* vt = a.v_tail + (size_t)bg * TILE * d0;
+    // scores: lane owns tokens lane and lane + 64
+    float sc[2][GM];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = lane + 64 * u;
+#pragma unroll
+        for (int n = 0; n < GM; ++n) sc[u][n] = 0.0f;
+        if (t < T) {
+            for (int j = 0; j < d0; j += 8) {
+                const uint4 w = *reinterpret_cast<const uint4*>(kt + (size_t)t * d0 + j);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float kv = h2f_bits((uint16_t)((e & 1) ? (ws[e >> 1] >> 16) : (ws[e >> 1] & 0xFFFF)));
+#pragma unroll
+                    for (int n = 0; n < GM; ++n)
+                        if (n < G) sc[u][n] = __builtin_fmaf(qs[n * D + j + e], kv, sc[u][n]);
+                }
+            }
+        }
+    }
+    float m[GM], l[GM];
+#pragma unroll
+    for (int n = 0; n < GM; ++n) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            if (lane + 64 * u < T) mx = fmaxf(mx, a.sm_scale * sc[u][n]);
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float sum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = lane + 64 * u;
+            const float pv = (t < T) ? expf(a.sm_scale * sc[u][n] - mx) : 0.0f;
+            ps[t * GM + n] = pv;
+            sum += pv;
+        }
+        for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+        m[n] = mx;
+        l[n] = sum;
+    }
+    __syncthreads();
+    // acc[n][j] = sum_t p[t][n] v[t][j]: lane owns channels lane + 64 r
+    for (int j = lane; j < D; j += 64) {
+        float acc[GM];
+#pragma unroll
+        for (int n = 0; n < GM; ++n) acc[n] = 0.0f;
+        if (j < d0) {
+            for (int t = 0; t < T; ++t) {
+                const float vv = h2f_bits(vt[(size_t)t * d0 + j]);
+#pragma unroll
+                for (int n = 0; n < GM; ++n) acc[n] = __builtin_fmaf(ps[t * GM + n], vv, acc[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < GM; ++n) os[n * D + j] = acc[n];
+    }
+    __syncthreads();
+    // rotate each query's acc: H acc / sqrt(D)
+    for (int h = 1; h < D; h <<= 1) {
+        for (int k = lane; k < G * D / 2; k += 64) {
+            const int r = k / (D / 2), pidx = k % (D / 2);
+            const int lo = (pidx / h) * 2 * h + (pidx % h), hi = lo + h;
+            const float x = os[r * D + lo], y = os[r * D + hi];
+            os[r * D + lo] = x + y;
+            os[r * D + hi] = x - y;
+        }
+        __syncthreads();
+    }
+    const float rs = 1.0f / __builtin_sqrtf((float)D);
+    for (int k = lane; k < G * (D + 2); k += 64) {
+        const int n = k / (D + 2), e = k % (D + 2);
+        float v;
+        if (e == 0) v = m[0];
+        else if (e == 1) v = l[0];
+        else v = os[n * D + e - 2] * rs;
+        if (e < 2) {
+            // m, l of query n (held by every lane)
+#pragma unroll
+            for (int nn = 0; nn < GM; ++nn)
+                if (nn == n) v = (e == 0) ? m[nn] : l[nn];
+        }
+        part(n)[e] = v;
+    }
+}
+
 __global__ void fill_zero_kernel(float* out, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = 0.0f;
@@ -585,16 +725,24 @@ __global__ void fill_zero_kernel(float* out, int64_t n) {
 template <int D, int KB, int VB, int GMAX>
 static hipError_t launch_att(const AttnArgs& a, hipStream_t s) {
     const int G = a.n_q_heads / a.n_kv_heads;
-    const int per_wave = AttnLds<D>::bytes(G);
-    int wpb = 65536 / per_wave;
-    if (wpb > 4) wpb = 4;
-    if (wpb < 1) wpb = 1;
-    const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
-    const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
-    hipLaunchKernelGGL((attn_partial_kernel<D, KB, VB, GMAX>), dim3((unsigned)blocks),
-                       dim3(64 * wpb), (size_t)per_wave * wpb, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (a.n_splits > 0) {
+        const int per_wave = AttnLds<D>::bytes(G);
+        int wpb = 65536 / per_wave;
+        if (wpb > 4) wpb = 4;
+        if (wpb < 1) wpb = 1;
+        const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
+        const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
+        hipLaunchKernelGGL((attn_partial_kernel<D, KB, VB, GMAX>), dim3((unsigned)blocks),
+                           dim3(64 * wpb), (size_t)per_wave * wpb, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.tail_len) {
+        hipLaunchKernelGGL((attn_tail_kernel<D>), dim3((unsigned)(a.batch * a.n_kv_heads)),
+                           dim3(64), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(a.batch * a.n_q_heads)),
                        dim3(256), 0, s, a);
     return hipGetLastError();
@@ -616,7 +764,7 @@ static hipError_t launch_att_bits(const AttnArgs& a, int kb, int vb, hipStream_t
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_t s) {
-    if (a.tiles_per_seq == 0) {
+    if (a.tiles_per_seq == 0 && !a.tail_len) {
         const int64_t n = (int64_t)a.batch * a.n_q_heads * a.d0;
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            a.out, n);

@@ -18,6 +18,8 @@ struct QuantArgs {
     int64_t n_v;        // tiles of V to process (0 = skip V)
     int d0;
     int n_iters;
+    const int64_t* dst = nullptr;   // output slot of input tile i (nullptr: slot i)
+    int64_t pool = 0;               // slots in the output arrays when dst is set
 };
 
 struct DequantArgs {
@@ -44,10 +46,18 @@ struct AttnArgs {
     int n_q_heads;
     int n_kv_heads;
     int tiles_per_seq;
-    int n_splits;        // splits per (b, g)
+    int n_splits;        // splits per (b, g) of the packed tiles
     int tiles_per_split;
     int d0;
     float sm_scale;
+    int n_parts = 0;     // partial slots per (b, h) in the workspace (n_splits, + 1 with a tail)
+    // paged cache (table == nullptr: tile i of (b, g) at (b * n_kv_heads + g) * tiles_per_seq + i)
+    const int32_t* table = nullptr;     // [batch][tiles_per_seq] physical block ids
+    const int32_t* nblk = nullptr;      // [batch] used blocks
+    const int32_t* tail_len = nullptr;  // [batch] fp16 tail tokens
+    const uint16_t* k_tail = nullptr;   // [batch][n_kv_heads][128][d0]
+    const uint16_t* v_tail = nullptr;
+    int64_t pool_blocks = 0;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int D, int kb, int vb, hipStream_t s);
@@ -58,6 +68,6 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_
 // query and the launch, so both agree).
 void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
                     int* tiles_per_split);
-size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_splits);
+size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 
 }  // namespace kvarn

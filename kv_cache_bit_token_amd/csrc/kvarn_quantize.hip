@@ -443,15 +443,23 @@ template <int D, int KB, int VB, bool FULL>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
     __shared__ __align__(16) float lds[quant_lds_floats<D>()];
     const int64_t tile = blockIdx.x;
-    if (tile < args.n_k) {
-        quantize_tile<D, KB, true, FULL>(args.k + tile * TILE * args.d0, args.d0, args.n_iters,
-                                   args.kc + tile * (TILE * D * KB / 8),
-                                   args.km + tile * (2 * D + TILE), lds);
+    const bool is_k = tile < args.n_k;
+    const int64_t src = is_k ? tile : tile - args.n_k;
+    // output slot: the tile itself, or its entry of dst (out-of-range entries
+    // skip the tile; the test is uniform over the workgroup)
+    int64_t slot = src;
+    if (args.dst) {
+        slot = args.dst[src];
+        if (slot < 0 || slot >= args.pool) return;
+    }
+    if (is_k) {
+        quantize_tile<D, KB, true, FULL>(args.k + src * TILE * args.d0, args.d0, args.n_iters,
+                                         args.kc + slot * (TILE * D * KB / 8),
+                                         args.km + slot * (2 * D + TILE), lds);
     } else {
-        const int64_t vt = tile - args.n_k;
-        quantize_tile<D, VB, false, FULL>(args.v + vt * TILE * args.d0, args.d0, args.n_iters,
-                                    args.vc + vt * (TILE * D * VB / 8),
-                                    args.vm + vt * (2 * TILE + D), lds);
+        quantize_tile<D, VB, false, FULL>(args.v + src * TILE * args.d0, args.d0, args.n_iters,
+                                          args.vc + slot * (TILE * D * VB / 8),
+                                          args.vm + slot * (2 * TILE + D), lds);
     }
 }
 

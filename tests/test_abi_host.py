@@ -130,6 +130,47 @@ def test_attention_validation_without_launch():
     assert at(ctypes.byref(P(head_dim=7)), 64, 32, 8, 256, A, A, A, A, A, 0.1, A, A, need, None) == 2
 
 
+def test_quantize_to_validation_without_launch():
+    lib = _lib.load()
+    q = lib.kvarn_quantize_tiles_to
+    ok = ctypes.byref(P())
+    assert q(ok, 0, A, A, A, 4, A, A, A, A, None) == 0          # nothing to do
+    assert q(ok, 3, A, A, A, 0, A, A, A, A, None) == 0          # empty pool: every tile skipped
+    assert q(ok, 3, None, None, None, 4, None, None, None, None, None) == 0
+    assert q(ok, 3, A, A, None, 4, A, A, A, A, None) == 1       # no destination table
+    assert q(ok, 3, A, A, A, -1, A, A, A, A, None) == 6
+    assert q(ok, -3, A, A, A, 4, A, A, A, A, None) == 6
+    assert q(ok, 3, A, A, MIS, 4, A, A, A, A, None) == 7
+    assert q(ok, 3, A, None, A, 4, A, A, A, A, None) == 1       # V set partly NULL
+    assert q(ctypes.byref(P(it=-1)), 3, A, A, A, 4, A, A, A, A, None) == 5
+
+
+def test_paged_attention_validation_without_launch():
+    lib = _lib.load()
+    ws = lib.kvarn_decode_attention_paged_workspace
+    nb = ctypes.c_size_t()
+    ok = ctypes.byref(P())
+    assert ws(ok, 16, 32, 8, 256, ctypes.byref(nb)) == 0 and nb.value > 0
+    need = nb.value
+    assert ws(ok, 16, 32, 8, 0, ctypes.byref(nb)) == 0 and 0 < nb.value < need   # tail slot only
+    assert ws(ok, 16, 32, 8, -1, ctypes.byref(nb)) == 6
+    assert ws(ok, 16, 31, 8, 4, ctypes.byref(nb)) == 6
+    assert ws(ok, 16, 32, 8, 4, None) == 1
+    at = lib.kvarn_decode_attention_paged
+    args = lambda **kw: [kw.get("p", ok), kw.get("batch", 16), 32, 8, 256, kw.get("pool", 100),
+                         kw.get("table", A), A, kw.get("tail", A), A, A, A, A, A,
+                         kw.get("kt", A), A, 0.1, A, kw.get("ws", A), kw.get("wsb", need), None]
+    assert at(*args(batch=0)) == 0                                 # empty batch: no launch
+    assert at(*args(tail=None)) == 1
+    assert at(*args(kt=None)) == 1
+    assert at(*args(table=None)) == 1                              # pool present, table missing
+    assert at(*args(ws=None)) == 1
+    assert at(*args(wsb=need - 8)) == 8
+    assert at(*args(pool=-5)) == 6
+    assert at(*args(table=MIS)) == 7
+    assert at(*args(p=ctypes.byref(P(head_dim=300)))) == 2
+
+
 def test_status_strings():
     lib = _lib.load()
     for code in range(10):
@@ -137,7 +178,8 @@ def test_status_strings():
     assert lib.kvarn_status_str(42) == b"unknown status"
 
 
-@pytest.mark.parametrize("name", ["quantize_tiles", "dequantize_tiles", "decode_attention"])
+@pytest.mark.parametrize("name", ["quantize_tiles", "dequantize_tiles", "decode_attention",
+                                  "quantize_tiles_to", "decode_attention_paged"])
 def test_python_api_refuses_cpu_tensors(name):
     import torch
     import kv_cache_bit_token_amd as kv
@@ -149,8 +191,19 @@ def test_python_api_refuses_cpu_tensors(name):
             c = torch.zeros(1, 8192, dtype=torch.uint8)
             m = torch.zeros(1, 384, dtype=torch.float16)
             kv.dequantize_tiles(c, c, m, m, head_dim=128)
-        else:
+        elif name == "decode_attention":
             c = torch.zeros(1, 8192, dtype=torch.uint8)
             m = torch.zeros(1, 384, dtype=torch.float16)
             kv.decode_attention(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m,
                                 n_kv_heads=1, tiles_per_seq=1)
+        elif name == "quantize_tiles_to":
+            c = torch.zeros(2, 8192, dtype=torch.uint8)
+            m = torch.zeros(2, 384, dtype=torch.float16)
+            kv.quantize_tiles_to(x, x, torch.zeros(1, dtype=torch.int64), c, c, m, m)
+        else:
+            c = torch.zeros(1, 8192, dtype=torch.uint8)
+            m = torch.zeros(1, 384, dtype=torch.float16)
+            i = torch.zeros(1, 1, dtype=torch.int32)
+            t = torch.zeros(1, 1, 128, 128, dtype=torch.float16)
+            kv.decode_attention_paged(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m, i,
+                                      i[0], i[0], t, t, n_kv_heads=1)
