@@ -139,6 +139,64 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def paged_attention_measure(kv, kc, vc, km, vm, q, reps=20):
+    """Decode attention over the same packed cache laid out as a paged pool
+    (shuffled physical blocks, one table row per layer) plus an fp16 tail of
+    1-127 tokens per (layer, KV head); timed with HIP events, outside the
+    step.  Bytes: the packed blocks, the tails' fp16 K and V, q and out."""
+    import numpy as np
+    import torch
+    from kv_cache_bit_token_amd import synthetic
+    from kv_cache_bit_token_amd.paged import paged_layout
+
+    dev = q.device
+    tps = TOKENS // 128
+    table, nb, tl, pool = paged_layout(7, LAYERS, tps, pool_blocks=LAYERS * tps, full=True)
+    # pool row p * KV_HEADS + g holds the tile (b * KV_HEADS + g) * tps + i of table[b][i] = p
+    src = np.empty(pool * KV_HEADS, np.int64)
+    for b in range(LAYERS):
+        for i in range(tps):
+            p = table[b, i]
+            for g in range(KV_HEADS):
+                src[p * KV_HEADS + g] = (b * KV_HEADS + g) * tps + i
+    idx = torch.from_numpy(src).to(dev)
+    pkc, pvc, pkm, pvm = (t.index_select(0, idx) for t in (kc, vc, km, vm))
+    kt, vt = synthetic.outlier_kv_torch(8, LAYERS * KV_HEADS, 128, HEAD_DIM, dev)
+    kt = kt.view(LAYERS, KV_HEADS, 128, HEAD_DIM)
+    vt = vt.view(LAYERS, KV_HEADS, 128, HEAD_DIM)
+    t_table = torch.from_numpy(table).to(dev)
+    t_nb, t_tl = torch.from_numpy(nb).to(dev), torch.from_numpy(tl).to(dev)
+    wsb = kv.decode_attention_paged_workspace(batch=LAYERS, n_q_heads=Q_HEADS, n_kv_heads=KV_HEADS,
+                                              max_blocks=tps, head_dim=HEAD_DIM)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((LAYERS, Q_HEADS, HEAD_DIM), dtype=torch.float32, device=dev)
+
+    def run():
+        kv.decode_attention_paged(q, pkc, pvc, pkm, pvm, t_table, t_nb, t_tl, kt, vt,
+                                  n_kv_heads=KV_HEADS, workspace=ws, out=out)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    b = per_tile_bytes(HEAD_DIM)
+    packed = int(nb.sum()) * KV_HEADS * b["packed_pair"]
+    tail = int(tl.sum()) * KV_HEADS * 2 * HEAD_DIM * 2
+    nbytes = packed + tail + LAYERS * Q_HEADS * HEAD_DIM * (2 + 4)
+    tokens = (int(nb.sum()) * 128 + int(tl.sum())) * KV_HEADS
+    return {"ms": round(ms, 4), "hbm_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / HBM_PEAK, 4),
+            "fp16_equiv_GBps": round(tokens * HEAD_DIM * 4 / (ms / 1e3) / 1e9, 1),
+            "workload": "64 sequences x 8 KV heads x (128 shuffled pool blocks + 1-127 fp16 tail "
+                        "tokens), GQA 32/8, K4V2; outside the timed step"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +204,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=LAYERS * KV_HEADS,
                     help="(layer, head) sequences in the CPU-oracle sample; 0 skips it")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache decode-attention measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -255,6 +315,8 @@ def main():
                      "hbm_frac": stages["quantize"]["hbm_frac"]},
         "wall_s": round(t_wall, 3),
     }
+    if not args.no_paged:
+        result["paged_decode_attention"] = paged_attention_measure(kv, kc, vc, km, vm, q)
     if args.cpu_seqs > 0:
         result["cpu_baseline"] = cpu_baseline(k, v, q, args.cpu_seqs)
     print(json.dumps(result), flush=True)

@@ -598,19 +598,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 }
 
 // ---- fp16 tail of a paged sequence (at most 128 tokens, not yet a tile) ----
-// One 64-lane workgroup per (b, KV head): plain fp32 attention of the group's
-// query heads over the tail's fp16 K and V, in the original channel domain
-// (the scores are the same in either domain, the rotation being orthonormal).
-// Its partial (m, l, acc) goes to the last slot of the workspace with acc
-// rotated (H acc / sqrt(D)), so that the combine kernel's final rotation
-// returns it to the original domain together with the packed tiles' slots.
-template <int D>
-__global__ __launch_bounds__(64) void attn_tail_kernel(AttnArgs a) {
-    constexpr int GM = 16;
-    __shared__ float qs[GM * D];
-    __shared__ float ps[TILE * GM];
-    __shared__ float os[GM * D];
-    const int lane = threadIdx.x;
+// One 256-thread workgroup per (b, KV head): plain fp32 attention of the
+// group's query heads over the tail's fp16 K and V, in the original channel
+// domain (the scores are the same in either domain, the rotation being
+// orthonormal).  Its partial (m, l, acc) goes to the last slot of the
+// workspace with acc rotated (H acc / sqrt(D)), so that the combine kernel's
+// final rotation returns it to the original domain together with the packed
+// tiles' slots.  Query rows GM > G are zero and their results are dropped.
+//   scores: thread pair (2t, 2t+1) holds token t, one half of the channels
+//           each, every 16-byte load of the half in flight;
+//   p . V:  thread (s, c) sums tokens s, s + NS, ... over channel chunk c
+//           (8 channels, one 16-byte load per token); the NS token slices
+//           are reduced across lanes, then across the four waves in LDS.
+template <int D, int GM>
+__global__ __launch_bounds__(256) void attn_tail_kernel(AttnArgs a) {
+    constexpr int NT = 256;
+    constexpr int HC = D / 2;                      // channels per score thread
+    constexpr int CPR = D / 8;                     // 16-byte chunks of a padded row
+    constexpr int NS = NT / CPR;                   // token slices of the p . V phase
+    constexpr int TPS = TILE / NS;                 // tokens per slice
+    constexpr int SPW = 64 / CPR;                  // slices per wave
+    __shared__ __align__(16) float qs[GM * D];     // q; then the summed acc
+    __shared__ __align__(16) float ps[TILE * GM];  // p[t][n]
+    __shared__ float red[2][4][GM];                // per-wave max and sum
+    __shared__ float ml[2][GM];                    // final m and l
+    float* os = qs;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int bg = blockIdx.x;
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int G = a.n_q_heads / a.n_kv_heads;
@@ -621,79 +634,123 @@ __global__ __launch_bounds__(64) void attn_tail_kernel(AttnArgs a) {
         return a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + slot) * (D + 2);
     };
     if (T == 0) {
-        for (int k = lane; k < G * (D + 2); k += 64) part(k / (D + 2))[k % (D + 2)] = (k % (D + 2) == 0) ? -INFINITY : 0.0f;
+        for (int k = tid; k < G * (D + 2); k += NT)
+            part(k / (D + 2))[k % (D + 2)] = (k % (D + 2) == 0) ? -INFINITY : 0.0f;
         return;
     }
-    for (int k = lane; k < G * D; k += 64) {
+    for (int k = tid; k < GM * D; k += NT) {
         const int n = k / D, j = k % D;
-        qs[k] = (j < d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + g * G + n) * d0 + j]) : 0.0f;
+        qs[k] = (n < G && j < d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + g * G + n) * d0 + j]) : 0.0f;
     }
     __syncthreads();
     const uint16_t* kt = a.k_tail + (size_t)bg * TILE * d0;
     const uint16_t* vt = a.v_tail + (size_t)bg * TILE * d0;
-    // scores: lane owns tokens lane and lane + 64
-    float sc[2][GM];
+
+    // scores
+    const int t = tid >> 1, h = tid & 1;
+    float sc[GM];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int t = lane + 64 * u;
+    for (int n = 0; n < GM; ++n) sc[n] = 0.0f;
+    if (t < T) {
+        uint4 w[HC / 8];
 #pragma unroll
-        for (int n = 0; n < GM; ++n) sc[u][n] = 0.0f;
-        if (t < T) {
-            for (int j = 0; j < d0; j += 8) {
-                const uint4 w = *reinterpret_cast<const uint4*>(kt + (size_t)t * d0 + j);
-                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        for (int c = 0; c < HC / 8; ++c) {
+            const int j = h * HC + 8 * c;
+            w[c] = (j < d0) ? *reinterpret_cast<const uint4*>(kt + (size_t)t * d0 + j)
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float kv = h2f_bits((uint16_t)((e & 1) ? (ws[e >> 1] >> 16) : (ws[e >> 1] & 0xFFFF)));
+        for (int c = 0; c < HC / 8; ++c) {
+            const uint32_t wd[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
 #pragma unroll
-                    for (int n = 0; n < GM; ++n)
-                        if (n < G) sc[u][n] = __builtin_fmaf(qs[n * D + j + e], kv, sc[u][n]);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float kv = h2f_bits((uint16_t)((e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xFFFF)));
+                const int j = h * HC + 8 * c + e;
+#pragma unroll
+                for (int n = 0; n < GM; ++n) sc[n] = __builtin_fmaf(qs[n * D + j], kv, sc[n]);
             }
         }
     }
-    float m[GM], l[GM];
+#pragma unroll
+    for (int n = 0; n < GM; ++n) sc[n] = a.sm_scale * (sc[n] + __shfl_xor(sc[n], 1));
+
+    // softmax statistics over the T tokens (each token is held by two lanes)
 #pragma unroll
     for (int n = 0; n < GM; ++n) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            if (lane + 64 * u < T) mx = fmaxf(mx, a.sm_scale * sc[u][n]);
+        float mx = (t < T) ? sc[n] : -INFINITY;
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        float sum = 0.0f;
+        if (lane == 0) red[0][wv][n] = mx;
+    }
+    __syncthreads();
+    float pn[GM];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = lane + 64 * u;
-            const float pv = (t < T) ? expf(a.sm_scale * sc[u][n] - mx) : 0.0f;
-            ps[t * GM + n] = pv;
-            sum += pv;
-        }
+    for (int n = 0; n < GM; ++n) {
+        const float mx = fmaxf(fmaxf(red[0][0][n], red[0][1][n]), fmaxf(red[0][2][n], red[0][3][n]));
+        pn[n] = (t < T) ? exp2f((sc[n] - mx) * kLog2e) : 0.0f;
+        float sum = h ? 0.0f : pn[n];
         for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-        m[n] = mx;
-        l[n] = sum;
+        if (lane == 0) red[1][wv][n] = sum;
+        if (tid == 0) ml[0][n] = mx;
+    }
+    if (h == 0) {
+#pragma unroll
+        for (int n = 0; n < GM; ++n) ps[t * GM + n] = pn[n];
     }
     __syncthreads();
-    // acc[n][j] = sum_t p[t][n] v[t][j]: lane owns channels lane + 64 r
-    for (int j = lane; j < D; j += 64) {
-        float acc[GM];
+    if (tid < GM) ml[1][tid] = (red[1][0][tid] + red[1][1][tid]) + (red[1][2][tid] + red[1][3][tid]);
+
+    // p . V
+    const int c = tid % CPR, sl = tid / CPR;
+    const bool cok = 8 * c < d0;
+    uint4 v[TPS];
 #pragma unroll
-        for (int n = 0; n < GM; ++n) acc[n] = 0.0f;
-        if (j < d0) {
-            for (int t = 0; t < T; ++t) {
-                const float vv = h2f_bits(vt[(size_t)t * d0 + j]);
+    for (int i = 0; i < TPS; ++i) {
+        const int tt = sl + NS * i;
+        v[i] = (cok && tt < T) ? *reinterpret_cast<const uint4*>(vt + (size_t)tt * d0 + 8 * c)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float acc[GM][8];
 #pragma unroll
-                for (int n = 0; n < GM; ++n) acc[n] = __builtin_fmaf(ps[t * GM + n], vv, acc[n]);
-            }
+    for (int n = 0; n < GM; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[n][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+        const int tt = sl + NS * i;
+        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float vv = h2f_bits((uint16_t)((e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xFFFF)));
+#pragma unroll
+            for (int n = 0; n < GM; ++n) acc[n][e] = __builtin_fmaf(ps[tt * GM + n], vv, acc[n][e]);
         }
-#pragma unroll
-        for (int n = 0; n < GM; ++n) os[n * D + j] = acc[n];
     }
-    __syncthreads();
+    // slices of one wave: lanes c + CPR k
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int n = 0; n < GM; ++n)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[n][e] += __shfl_xor(acc[n][e], o);
+    // waves in turn (q is dead: every thread passed the statistics barriers)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (wv == w && lane < CPR) {
+#pragma unroll
+            for (int n = 0; n < GM; ++n)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    os[n * D + 8 * c + e] = (w == 0) ? acc[n][e] : os[n * D + 8 * c + e] + acc[n][e];
+        }
+        __syncthreads();
+    }
+    static_assert(SPW >= 1 && NS * CPR == NT, "tail thread mapping");
     // rotate each query's acc: H acc / sqrt(D)
-    for (int h = 1; h < D; h <<= 1) {
-        for (int k = lane; k < G * D / 2; k += 64) {
+#pragma unroll
+    for (int hs = 1; hs < D; hs <<= 1) {
+        for (int k = tid; k < G * (D / 2); k += NT) {
             const int r = k / (D / 2), pidx = k % (D / 2);
-            const int lo = (pidx / h) * 2 * h + (pidx % h), hi = lo + h;
+            const int lo = (pidx / hs) * 2 * hs + (pidx % hs), hi = lo + hs;
             const float x = os[r * D + lo], y = os[r * D + hi];
             os[r * D + lo] = x + y;
             os[r * D + hi] = x - y;
@@ -701,19 +758,9 @@ __global__ __launch_bounds__(64) void attn_tail_kernel(AttnArgs a) {
         __syncthreads();
     }
     const float rs = 1.0f / __builtin_sqrtf((float)D);
-    for (int k = lane; k < G * (D + 2); k += 64) {
+    for (int k = tid; k < G * (D + 2); k += NT) {
         const int n = k / (D + 2), e = k % (D + 2);
-        float v;
-        if (e == 0) v = m[0];
-        else if (e == 1) v = l[0];
-        else v = os[n * D + e - 2] * rs;
-        if (e < 2) {
-            // m, l of query n (held by every lane)
-#pragma unroll
-            for (int nn = 0; nn < GM; ++nn)
-                if (nn == n) v = (e == 0) ? m[nn] : l[nn];
-        }
-        part(n)[e] = v;
+        part(n)[e] = (e >= 2) ? os[n * D + e - 2] * rs : ml[e][n];
     }
 }
 
@@ -738,8 +785,8 @@ static hipError_t launch_att(const AttnArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (a.tail_len) {
-        hipLaunchKernelGGL((attn_tail_kernel<D>), dim3((unsigned)(a.batch * a.n_kv_heads)),
-                           dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attn_tail_kernel<D, GMAX>), dim3((unsigned)(a.batch * a.n_kv_heads)),
+                           dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
