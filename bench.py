@@ -64,14 +64,19 @@ def quant_ops_per_elem(D, n_iters):
 
 # HBM bytes per launch of the quantiser on this workload, from rocprofv3
 # FETCH_SIZE / WRITE_SIZE (scaled by the copy calibration), and the SHA-256
-# prefix of the kernel source they were taken for.
-QUANT_TRAFFIC = {"source_sha256": "6920e17daa51c78e", "fetch_bytes": 4295772351, "write_bytes": 905969664}
-QUANT_SOURCE = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", "kvarn_quantize.hip")
+# prefix of the kernel sources (kernel file + shared device header) they were
+# taken for.
+QUANT_TRAFFIC = {"source_sha256": "a3eff37653832368", "fetch_bytes": 4295729131, "write_bytes": 905969664}
+QUANT_SOURCE = [os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", f)
+                for f in ("kvarn_quantize.hip", "kvarn_device.hpp")]
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def per_tile_bytes(D):
