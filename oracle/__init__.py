@@ -58,6 +58,8 @@ def _load():
         "oracle_decode_attention_paged": (None, [_int, _int, _int, _int, _int, _int, _int, _i32p,
                                                  _i32p, _i32p, _u16p, _u8p, _u8p, _u16p, _u16p,
                                                  _u16p, _u16p, ctypes.c_double, _dp]),
+        "oracle_decode_attention_fp16": (None, [_int, _int, _int, _i64, _int, _u16p, _u16p, _u16p,
+                                                ctypes.c_double, _dp]),
         "oracle_set_threads": (None, [_int]),
         "oracle_max_threads": (_int, []),
     }
@@ -273,4 +275,21 @@ def decode_attention_paged(q16, k_codes, v_codes, k_meta16, v_meta16, block_tabl
         bt.ctypes.data_as(_i32p), nb.ctypes.data_as(_i32p), tl.ctypes.data_as(_i32p),
         _ptr(q, _u16p), _ptr(kc, _u8p), _ptr(vc, _u8p), _ptr(km, _u16p), _ptr(vm, _u16p),
         _ptr(kt, _u16p), _ptr(vt, _u16p), float(sm_scale), _ptr(out, _dp))
+    return out
+
+
+def decode_attention_fp16(q16, k16, v16, *, sm_scale: float = None):
+    """Attention over an uncompressed fp16 cache.  q [batch][n_q_heads][d0],
+    k / v [batch][n_kv_heads][seq_len][d0] float16 -> [batch][n_q_heads][d0] f64."""
+    q = _h(q16)
+    batch, hq, d0 = q.shape
+    k, v = _h(k16), _h(v16)
+    assert k.ndim == 4 and k.shape[0] == batch and k.shape[3] == d0 and v.shape == k.shape
+    hkv, seq = k.shape[1], k.shape[2]
+    assert hq % hkv == 0
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d0)
+    out = np.empty((batch, hq, d0), np.float64)
+    _load().oracle_decode_attention_fp16(batch, hq, hkv, seq, d0, _ptr(q, _u16p), _ptr(k, _u16p),
+                                         _ptr(v, _u16p), float(sm_scale), _ptr(out, _dp))
     return out

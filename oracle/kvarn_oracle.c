@@ -611,3 +611,39 @@ void oracle_decode_attention_paged(int batch, int n_q_heads, int n_kv_heads, int
         free(sc);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over an uncompressed binary16 cache: the baseline that   */
+/* the quantised cache is measured against (hotdry page, section on the      */
+/* deployment parameters: throughput is compared with an FP16 baseline; deep */
+/* page, section on where the memory of a 16K-context inference goes: each  */
+/* decode step reads the whole cache).  Plain softmax attention in double    */
+/* over the binary16 values taken as they are.                               */
+/* k, v: [batch][n_kv_heads][seq_len][d0] binary16; q: [batch][n_q_heads][d0] */
+/* binary16; out: [batch][n_q_heads][d0] double.  seq_len 0 gives out = 0.   */
+/* ------------------------------------------------------------------------ */
+void oracle_decode_attention_fp16(int batch, int n_q_heads, int n_kv_heads, int64_t seq_len,
+                                  int d0, const uint16_t *q, const uint16_t *k,
+                                  const uint16_t *v, double sm_scale, double *out)
+{
+    int group = n_q_heads / n_kv_heads;
+    int64_t T = seq_len;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)batch * n_kv_heads; ++bg) {
+        int b = (int)(bg / n_kv_heads), g = (int)(bg % n_kv_heads);
+        double *K = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *V = malloc((size_t)(T > 0 ? T : 1) * d0 * sizeof(double));
+        double *sc = malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+        const uint16_t *kb = k + (size_t)bg * T * d0;
+        const uint16_t *vb = v + (size_t)bg * T * d0;
+        for (int64_t e = 0; e < T * d0; ++e) {
+            K[e] = oracle_half_to_double(kb[e]);
+            V[e] = oracle_half_to_double(vb[e]);
+        }
+        oracle_attend_group(q + (size_t)b * n_q_heads * d0, g, group, T, d0, K, V, sm_scale, sc,
+                            out + (size_t)b * n_q_heads * d0);
+        free(K);
+        free(V);
+        free(sc);
+    }
+}
