@@ -202,6 +202,44 @@ def paged_attention_measure(kv, kc, vc, km, vm, q, reps=20):
                         "tokens), GQA 32/8, K4V2; outside the timed step"}
 
 
+def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
+    """Decode attention over the uncompressed fp16 cache of the same workload
+    (the baseline of the pages' throughput comparison), timed with HIP events
+    outside the step.  Bytes: the fp16 K and V, q and out.  Also reports the
+    packed path's speed-up over it and the relative L2 distance between the
+    two attention outputs."""
+    import torch
+
+    kk = k.view(LAYERS, KV_HEADS, TOKENS, HEAD_DIM)
+    vv = v.view(LAYERS, KV_HEADS, TOKENS, HEAD_DIM)
+    wsb = kv.decode_attention_fp16_workspace(batch=LAYERS, n_q_heads=Q_HEADS, n_kv_heads=KV_HEADS,
+                                             seq_len=TOKENS, head_dim=HEAD_DIM)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty((LAYERS, Q_HEADS, HEAD_DIM), dtype=torch.float32, device=q.device)
+
+    def run():
+        kv.decode_attention_fp16(q, kk, vv, workspace=ws, out=out)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * k.numel() * 2 + LAYERS * Q_HEADS * HEAD_DIM * (2 + 4)
+    rel = float((packed_out - out).norm() / out.norm())
+    return {"ms": round(ms, 4), "hbm_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / HBM_PEAK, 4),
+            "packed_speedup": round(ms / packed_ms, 3),
+            "packed_rel_l2": round(rel, 6),
+            "workload": "same 64 x 8 x 16384 x 128 cache and queries, uncompressed fp16; "
+                        "outside the timed step"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +249,8 @@ def main():
                     help="(layer, head) sequences in the CPU-oracle sample; 0 skips it")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode-attention measurement")
+    ap.add_argument("--no-fp16", action="store_true",
+                    help="skip the fp16-cache decode-attention baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -320,6 +360,9 @@ def main():
                      "hbm_frac": stages["quantize"]["hbm_frac"]},
         "wall_s": round(t_wall, 3),
     }
+    if not args.no_fp16:
+        result["fp16_decode_attention"] = fp16_attention_measure(
+            kv, k, v, q, out, stages["decode_attention"]["ms"])
     if not args.no_paged:
         result["paged_decode_attention"] = paged_attention_measure(kv, kc, vc, km, vm, q)
     if args.cpu_seqs > 0:

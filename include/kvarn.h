@@ -180,6 +180,37 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params *params, int32_t ba
                                           float sm_scale, float *out, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/* ---- uncompressed fp16 cache: the baseline the packed cache is measured
+ * against (hotdry page, section on the deployment parameters: throughput is
+ * compared with an FP16 baseline; deep page, section
+ * "一次 16K context 的推論，記憶體都花到哪去了": every decode step reads the
+ * whole cache, so decode is bound by memory bandwidth) ---- */
+
+/* Workspace (bytes) that kvarn_decode_attention_fp16 needs for this shape
+ * (0 when seq_len == 0). */
+kvarn_status kvarn_decode_attention_fp16_workspace(int32_t head_dim, int32_t batch,
+                                                   int32_t n_q_heads, int32_t n_kv_heads,
+                                                   int64_t seq_len, size_t *bytes);
+
+/* One decode step of GQA attention over an fp16 cache:
+ *   out[b][h] = softmax(sm_scale * q[b][h] . K[b][g]^T) V[b][g],  g = h / (n_q_heads / n_kv_heads)
+ *   head_dim    D0: 33..256, multiple of 8 (no padding is involved)
+ *   q           [batch][n_q_heads][head_dim] fp16, device
+ *   k_fp16, v_fp16 [batch][n_kv_heads][seq_len][head_dim] fp16, device, read
+ *               only; with seq_len = 128 * tiles_per_seq this is the tile
+ *               layout that kvarn_quantize_tiles reads
+ *   out         [batch][n_q_heads][head_dim] fp32, device, written
+ *   workspace   at least kvarn_decode_attention_fp16_workspace bytes, device,
+ *               scratch (may be NULL when seq_len == 0)
+ * seq_len == 0 gives out = 0.  The GQA group holds at most 16 heads, and one
+ * (sequence, KV head) of K holds at most 2^31 - 1 bytes
+ * (seq_len * head_dim * 2), else KVARN_E_SHAPE. */
+kvarn_status kvarn_decode_attention_fp16(int32_t head_dim, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t seq_len, const void *q_fp16,
+                                         const void *k_fp16, const void *v_fp16, float sm_scale,
+                                         float *out, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
 /* Static description of a status code. */
 const char *kvarn_status_str(kvarn_status status);
 

@@ -40,6 +40,10 @@ SIGNATURES = {
                                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                     ctypes.c_float, _vp, _vp, ctypes.c_size_t,
                                                     _vp]),
+    "kvarn_decode_attention_fp16_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i64,
+                                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "kvarn_decode_attention_fp16": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp,
+                                                   ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "kvarn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -261,3 +261,42 @@ def decode_attention_paged(q, k_codes, v_codes, k_meta, v_meta, block_table, n_b
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("kvarn_decode_attention_paged", st)
     return out
+
+
+def decode_attention_fp16_workspace(*, batch, n_q_heads, n_kv_heads, seq_len, head_dim):
+    lib = _lib.load()
+    nb = ctypes.c_size_t()
+    _check("kvarn_decode_attention_fp16_workspace",
+           lib.kvarn_decode_attention_fp16_workspace(int(head_dim), int(batch), int(n_q_heads),
+                                                     int(n_kv_heads), int(seq_len), ctypes.byref(nb)))
+    return nb.value
+
+
+def decode_attention_fp16(q, k, v, *, sm_scale=None, workspace=None, out=None):
+    """One decode step over an uncompressed fp16 cache (the baseline).
+
+    q: float16 [batch, n_q_heads, head_dim]; k, v: float16
+    [batch, n_kv_heads, seq_len, head_dim].  Returns float32 [batch, n_q_heads, head_dim].
+    """
+    _need_gpu(q, "q", torch.float16)
+    _need_gpu(k, "k", torch.float16)
+    _need_gpu(v, "v", torch.float16)
+    if k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[2]:
+        raise ValueError("k, v must be [batch, n_kv_heads, seq_len, head_dim] matching q")
+    batch, hq, head_dim = q.shape
+    n_kv, seq_len = k.shape[1], k.shape[2]
+    if sm_scale is None:
+        sm_scale = head_dim ** -0.5
+    nbytes = decode_attention_fp16_workspace(batch=batch, n_q_heads=hq, n_kv_heads=n_kv,
+                                             seq_len=seq_len, head_dim=head_dim)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, hq, head_dim), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    st = lib.kvarn_decode_attention_fp16(
+        int(head_dim), batch, hq, int(n_kv), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+        float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check("kvarn_decode_attention_fp16", st)
+    return out

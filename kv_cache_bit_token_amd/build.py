@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvarn.so")
-SOURCES = ["kvarn_abi.cpp", "kvarn_quantize.hip", "kvarn_dequantize.hip", "kvarn_attention.hip"]
+SOURCES = ["kvarn_abi.cpp", "kvarn_quantize.hip", "kvarn_dequantize.hip", "kvarn_attention.hip",
+           "kvarn_attention_fp16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -347,3 +347,72 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t ba
 }
 
 }  // extern "C"
+
+// ---- attention over an uncompressed fp16 cache (the baseline) ----
+
+static kvarn_status check_fp16_attention(int32_t head_dim, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t seq_len, int* D) {
+    if (head_dim < 33 || head_dim > 256 || (head_dim % 8) != 0) return KVARN_E_HEAD_DIM;
+    if (seq_len < 0) return KVARN_E_SHAPE;
+    // one (sequence, KV head) of K or V is addressed with 32-bit byte offsets
+    if (seq_len * head_dim * 2 > INT32_MAX) return KVARN_E_SHAPE;
+    kvarn_status st = check_attention_shape(batch, n_q_heads, n_kv_heads, 0);
+    if (st != KVARN_OK) return st;
+    if ((int64_t)batch * n_q_heads > INT32_MAX) return KVARN_E_SHAPE;
+    const int64_t tiles = (seq_len + TILE - 1) / TILE;
+    if (tiles > kMaxTiles || (int64_t)batch * n_kv_heads * tiles > kMaxTiles) return KVARN_E_SHAPE;
+    int d = 64;
+    while (d < head_dim) d *= 2;
+    *D = d;
+    return KVARN_OK;
+}
+
+kvarn_status kvarn_decode_attention_fp16_workspace(int32_t head_dim, int32_t batch,
+                                                   int32_t n_q_heads, int32_t n_kv_heads,
+                                                   int64_t seq_len, size_t* bytes) {
+    if (!bytes) return KVARN_E_NULL;
+    int D = 0;
+    kvarn_status st = check_fp16_attention(head_dim, batch, n_q_heads, n_kv_heads, seq_len, &D);
+    if (st != KVARN_OK) return st;
+    int ns = 0, sps = 0;
+    kvarn::attention_fp16_plan(batch, n_kv_heads, seq_len, D, &ns, &sps);
+    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns);
+    return KVARN_OK;
+}
+
+kvarn_status kvarn_decode_attention_fp16(int32_t head_dim, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t seq_len, const void* q_fp16,
+                                         const void* k_fp16, const void* v_fp16, float sm_scale,
+                                         float* out, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    int D = 0;
+    kvarn_status st = check_fp16_attention(head_dim, batch, n_q_heads, n_kv_heads, seq_len, &D);
+    if (st != KVARN_OK) return st;
+    if (!q_fp16 || !out) return KVARN_E_NULL;
+    if (seq_len > 0 && (!k_fp16 || !v_fp16 || !workspace)) return KVARN_E_NULL;
+    if (misaligned(q_fp16) || misaligned(out) || misaligned(k_fp16) || misaligned(v_fp16) ||
+        misaligned(workspace))
+        return KVARN_E_ALIGN;
+    int ns = 0, sps = 0;
+    kvarn::attention_fp16_plan(batch, n_kv_heads, seq_len, D, &ns, &sps);
+    if (ns > 0 && workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns))
+        return KVARN_E_WORKSPACE;
+    if (batch == 0) return KVARN_OK;
+
+    kvarn::Fp16AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q_fp16);
+    a.k = static_cast<const uint16_t*>(k_fp16);
+    a.v = static_cast<const uint16_t*>(v_fp16);
+    a.out = out;
+    a.ws = static_cast<float*>(workspace);
+    a.batch = batch;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.seq_len = seq_len;
+    a.n_splits = ns;
+    a.steps_per_split = sps;
+    a.d0 = head_dim;
+    a.sm_scale = sm_scale;
+    hipError_t e = kvarn::launch_attention_fp16(a, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVARN_OK : KVARN_E_HIP;
+}

@@ -60,6 +60,23 @@ struct AttnArgs {
     int64_t pool_blocks = 0;
 };
 
+// Decode attention over an uncompressed fp16 cache (the baseline).
+struct Fp16AttnArgs {
+    const uint16_t* q;   // [B][Hq][d0]
+    const uint16_t* k;   // [B][Hkv][seq_len][d0]
+    const uint16_t* v;
+    float* out;          // [B][Hq][d0]
+    float* ws;           // split-K partials [B][Hq][n_splits][D + 2]
+    int batch;
+    int n_q_heads;
+    int n_kv_heads;
+    int64_t seq_len;
+    int n_splits;        // splits per (b, g)
+    int steps_per_split; // token steps per split
+    int d0;
+    float sm_scale;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int D, int kb, int vb, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int D, int kb, int vb, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_t s);
@@ -69,5 +86,10 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_
 void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
                     int* tiles_per_split);
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
+
+// Split plan of the fp16-cache attention (token steps of 32 * 128 / D).
+void attention_fp16_plan(int batch, int n_kv_heads, int64_t seq_len, int D, int* n_splits,
+                         int* steps_per_split);
+hipError_t launch_attention_fp16(const Fp16AttnArgs& a, int D, hipStream_t s);
 
 }  // namespace kvarn

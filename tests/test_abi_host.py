@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "kvarn.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvarn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -171,6 +171,33 @@ def test_paged_attention_validation_without_launch():
     assert at(*args(p=ctypes.byref(P(head_dim=300)))) == 2
 
 
+def test_fp16_attention_validation_without_launch():
+    lib = _lib.load()
+    ws = lib.kvarn_decode_attention_fp16_workspace
+    nb = ctypes.c_size_t()
+    assert ws(128, 64, 32, 8, 32768, ctypes.byref(nb)) == 0 and nb.value > 0
+    need = nb.value
+    assert ws(128, 64, 32, 8, 0, ctypes.byref(nb)) == 0 and nb.value == 0
+    assert ws(130, 64, 32, 8, 100, ctypes.byref(nb)) == 2          # not a multiple of 8
+    assert ws(128, 64, 32, 8, -1, ctypes.byref(nb)) == 6
+    assert ws(128, 64, 32, 6, 100, ctypes.byref(nb)) == 6          # 32 % 6 != 0
+    assert ws(128, 1, 32, 1, 100, ctypes.byref(nb)) == 6           # group of 32 heads
+    assert ws(256, 1, 4, 1, 1 << 22, ctypes.byref(nb)) == 6        # 2 GiB of K per head
+    assert ws(128, 64, 32, 8, 100, None) == 1
+    at = lib.kvarn_decode_attention_fp16
+    args = lambda **kw: [kw.get("hd", 128), kw.get("batch", 64), 32, 8, kw.get("T", 32768),
+                         kw.get("q", A), kw.get("k", A), A, 0.1, kw.get("out", A),
+                         kw.get("ws", A), kw.get("wsb", need), None]
+    assert at(*args(batch=0)) == 0                                  # empty batch: no launch
+    assert at(*args(q=None)) == 1
+    assert at(*args(out=None)) == 1
+    assert at(*args(k=None)) == 1
+    assert at(*args(ws=None)) == 1
+    assert at(*args(wsb=need - 4)) == 8
+    assert at(*args(k=MIS)) == 7
+    assert at(*args(hd=300)) == 2
+
+
 def test_status_strings():
     lib = _lib.load()
     for code in range(10):
@@ -179,7 +206,8 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("name", ["quantize_tiles", "dequantize_tiles", "decode_attention",
-                                  "quantize_tiles_to", "decode_attention_paged"])
+                                  "quantize_tiles_to", "decode_attention_paged",
+                                  "decode_attention_fp16"])
 def test_python_api_refuses_cpu_tensors(name):
     import torch
     import kv_cache_bit_token_amd as kv
@@ -200,6 +228,9 @@ def test_python_api_refuses_cpu_tensors(name):
             c = torch.zeros(2, 8192, dtype=torch.uint8)
             m = torch.zeros(2, 384, dtype=torch.float16)
             kv.quantize_tiles_to(x, x, torch.zeros(1, dtype=torch.int64), c, c, m, m)
+        elif name == "decode_attention_fp16":
+            t = torch.zeros(1, 1, 128, 128, dtype=torch.float16)
+            kv.decode_attention_fp16(torch.zeros(1, 4, 128, dtype=torch.float16), t, t)
         else:
             c = torch.zeros(1, 8192, dtype=torch.uint8)
             m = torch.zeros(1, 384, dtype=torch.float16)

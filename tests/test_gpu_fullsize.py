@@ -196,3 +196,23 @@ def test_decode_attention_full_size():
     print("relative L2 vs fp16-cache attention:", max(errs))
     del k, v, kt, vt, kc, vc, km, vm
     _free()
+
+
+def test_decode_attention_fp16_full_size():
+    """The fp16-cache baseline at the decode-attention workload's size:
+    64 seq x 8 KV heads x 32768 tokens, GQA 32/8, sampled sequences checked
+    against the oracle's fp16-cache attention."""
+    B, n_kv, Hq, T, d0 = 64, 8, 32, 32768, 128
+    k, v = synthetic.outlier_kv_torch(5, B * n_kv, T, d0, DEV)
+    k, v = k.view(B, n_kv, T, d0), v.view(B, n_kv, T, d0)
+    q = synthetic.query_torch(5, B, Hq, d0, DEV)
+    out = kv.decode_attention_fp16(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    qh = q.cpu().numpy()
+    for b in (0, 29, 63):
+        ref = oracle.decode_attention_fp16(qh[b:b + 1], k[b:b + 1].cpu().numpy(),
+                                           v[b:b + 1].cpu().numpy())
+        print(b, compare_attention(out[b:b + 1].cpu().numpy(), ref))
+    del k, v
+    _free()
