@@ -136,3 +136,55 @@ def as_tiles(x):
     h, t, d0 = x.shape
     assert t % 128 == 0, "whole 128-token tiles only"
     return x.reshape(h * (t // 128), 128, d0)
+
+
+class FeedbackSource:
+    """Synthetic autoregressive token source for the error-accumulation probe.
+
+    Token t's query, key and value rows are fixed random projections of a
+    hidden vector x_t = unit-RMS(z_t + beta * unit-RMS(W_o . o_{t-1})), where z_t is
+    fresh N(0, 1) noise drawn from a per-step stream (numpy PCG64 seeded with
+    (seed, t), so every cache sees the same noise at step t) and o_{t-1} is
+    the previous step's attention output of the cache being driven.  The
+    feedback enters at a fixed share of the noise's energy (beta), so the
+    stream stays a mix of fresh and carried-over content.  An error in one
+    output therefore changes every later token, as in autoregressive
+    decoding.  Keys and values carry the outlier-channel
+    structure: K has n_ch channels with a large fixed offset of either sign
+    (|offset| ~ U(20, 50), the same for every token, so it shifts every score
+    of a query alike), V has n_ch channels scaled by U(20, 50); both rows
+    carry a per-token magnitude exp(tok_sigma * N(0, 1)).  Holds none of the
+    method's arithmetic.
+    """
+
+    def __init__(self, seed, d0, n_q_heads, beta=0.5, n_ch=4, ch_mult=(20.0, 50.0),
+                 tok_sigma=0.5):
+        rng = np.random.default_rng(seed)
+        self.seed, self.d0, self.hq = int(seed), int(d0), int(n_q_heads)
+        self.beta, self.tok_sigma = float(beta), float(tok_sigma)
+        self.wo = rng.standard_normal((d0, n_q_heads * d0)) / np.sqrt(n_q_heads * d0)
+        self.wk = rng.standard_normal((d0, d0)) / np.sqrt(d0)
+        self.wv = rng.standard_normal((d0, d0)) / np.sqrt(d0)
+        self.wq = rng.standard_normal((n_q_heads * d0, d0)) / np.sqrt(d0)
+        self.bk = np.zeros(d0)
+        self.bk[rng.choice(d0, n_ch, replace=False)] = (rng.uniform(*ch_mult, n_ch)
+                                                       * rng.choice([-1.0, 1.0], n_ch))
+        self.cv = np.ones(d0)
+        self.cv[rng.choice(d0, n_ch, replace=False)] = rng.uniform(*ch_mult, n_ch)
+
+    def token(self, t, o_prev=None):
+        """-> (q [n_q_heads][d0], k [d0], v [d0]) numpy float16 for step t;
+        o_prev: the previous attention output [n_q_heads][d0] (None at t = 0)."""
+        rng = np.random.default_rng([self.seed, int(t)])
+        x = rng.standard_normal(self.d0)
+        mag = np.exp(self.tok_sigma * rng.standard_normal())
+        if o_prev is not None:
+            fb = self.wo @ np.asarray(o_prev, np.float64).reshape(-1)
+            rms = np.sqrt(np.mean(fb * fb))
+            if rms > 0:
+                x = x + self.beta * fb / rms
+        x = x / np.sqrt(np.mean(x * x))
+        k = (self.wk @ x) * mag + self.bk
+        v = (self.wv @ x) * self.cv * mag
+        q = (self.wq @ x).reshape(self.hq, self.d0)
+        return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
