@@ -37,6 +37,7 @@
 // combine kernel merges the splits' (max, sum, acc) and undoes the rotation.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
+#include "kvarn_rsrc.hpp"
 
 namespace kvarn {
 
@@ -69,41 +70,71 @@ size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
 
 // ---- b-bit codes -> exact fp16 (code - 2^(b-1)) -----------------------------
 // A packed dword holds N = 32/b codes.  Pair k takes codes k and k + N/2 (bits
-// b*k and b*k + 16) into the two halves of a dword: shifted into the fp16
-// mantissa under a magic exponent (16 + c for b = 4, 4 + c for b = 2), then
-// the magic and the centre are subtracted with one packed fp16 add.
+// b*k and b*k + 16) into the two halves of a dword.  A code sitting at bit s
+// of its half (s + b <= 10) is OR-ed as it stands into the mantissa of a
+// magic fp16 whose unit in the last place is 2^-s, so the half reads
+// magic + code exactly; one packed fp16 add then subtracts magic + 2^(b-1).
+// Only the pairs whose bits lie above the mantissa need a shift, one shared
+// per dword: 4-bit pairs 0, 1 sit at s = 0, 4 and pairs 2, 3 at s = 0, 4 of
+// w >> 8; 2-bit pairs 0..4 at s = 0, 2, 4, 6, 8 and pairs 5..7 at s = 0, 2, 4
+// of w >> 10.
 template <int B> struct Codes;
 template <> struct Codes<4> {
-    static constexpr int N = 8, TB = 6;
-    static constexpr uint32_t MASK = 0x03C003C0u, MAGIC = 0x4C004C00u;
-    static constexpr float SUB = 24.0f, MID = 8.0f;
+    static constexpr int N = 8, SPLIT = 2, HI_SHIFT = 8;
+    static constexpr float MID = 8.0f;
 };
 template <> struct Codes<2> {
-    static constexpr int N = 16, TB = 8;
-    static constexpr uint32_t MASK = 0x03000300u, MAGIC = 0x44004400u;
-    static constexpr float SUB = 6.0f, MID = 2.0f;
+    static constexpr int N = 16, SPLIT = 5, HI_SHIFT = 10;
+    static constexpr float MID = 2.0f;
 };
 
+// (x & mask) | bits in one VALU operation (the compiler otherwise emits an
+// AND and an OR with literal operands); one scalar and one vector constant
+// respect the single scalar read of a VOP3 operation.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+    return r;
+}
+
+// The magic halves of the SPLIT bit positions, both halves of a dword, held
+// in vector registers for the whole kernel (made opaque to the compiler so it
+// does not rematerialise them at every use).
 template <int B>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, int k) {
+struct CodeMagic {
+    uint32_t m[Codes<B>::SPLIT];
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int i = 0; i < Codes<B>::SPLIT; ++i) {
+            const uint32_t f = (25u - (uint32_t)(B * i)) << 10;   // exponent field of 2^(10 - s)
+            asm volatile("v_mov_b32 %0, %1" : "=v"(m[i]) : "s"(f | (f << 16)));
+        }
+    }
+};
+
+// pair k of dword w (wh = w >> HI_SHIFT), as two fp16 values code - 2^(b-1)
+template <int B>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t wh, int k, const CodeMagic<B>& cm) {
     using C = Codes<B>;
-    const int sh = C::TB - B * k;
-    uint32_t x = sh >= 0 ? (w << sh) : (w >> (-sh));
-    x = (x & C::MASK) | C::MAGIC;
-    h2_t v = __builtin_bit_cast(h2_t, x);
-    v = v - (h2_t){(_Float16)C::SUB, (_Float16)C::SUB};
-    return __builtin_bit_cast(uint32_t, v);
+    const int i = k < C::SPLIT ? k : k - C::SPLIT;
+    const int s = B * i;                                      // bit of the code in its half
+    const uint32_t x = k < C::SPLIT ? w : wh;
+    const uint32_t mask = ((1u << B) - 1u) << s;
+    const uint32_t v = and_or(x, mask | (mask << 16), cm.m[i]);
+    const _Float16 sub = (_Float16)(-((float)(1 << (10 - s)) + C::MID));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v) + (h2_t){sub, sub});
 }
 
 // Matrix operand kb (4 fp16 values) out of a lane's run of packed dwords.
 // Operand kb uses dword d = kb / (N/4) and pairs 2*k2, 2*k2 + 1 (k2 = kb mod
 // N/4); element e holds code 2*k2 + (e >> 1) + (N/2)*(e & 1) of that dword.
 template <int B, int NW>
-__device__ __forceinline__ h4_t code_operand(const uint32_t (&w)[NW], int kb) {
+__device__ __forceinline__ h4_t code_operand(const uint32_t (&w)[NW], int kb, const CodeMagic<B>& cm) {
     constexpr int Q = Codes<B>::N / 4;
     const int d = kb / Q, k2 = kb % Q;
-    const uint32_t lo = code_pair<B>(w[d], 2 * k2);
-    const uint32_t hi = code_pair<B>(w[d], 2 * k2 + 1);
+    const uint32_t wh = w[d] >> Codes<B>::HI_SHIFT;
+    const uint32_t lo = code_pair<B>(w[d], wh, 2 * k2, cm);
+    const uint32_t hi = code_pair<B>(w[d], wh, 2 * k2 + 1, cm);
     return __builtin_bit_cast(h4_t, make_uint2(lo, hi));
 }
 
@@ -182,7 +213,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform (scalar), so the split's tile indices and table reads are too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int G = a.n_q_heads / a.n_kv_heads;
     const int GP = (G + 3) & ~3;
@@ -291,35 +323,39 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         if (blk < 0 || blk >= a.pool_blocks) blk = 0;
         return blk * a.n_kv_heads + g;
     };
+    // codes through per-tile buffer descriptors: per-lane offsets fixed, the
+    // block moves the scalar offset
+    const int kvo = mrow * KROW + mgrp * (KROW / 4);
+    const int vvo = mrow * VROW + mgrp * (VROW / 4);
     auto load_k = [&](int ti) {
-        const uint8_t* kc = a.kc + tile_index(ti) * KCB;
+        const auto r = make_rsrc(a.kc + tile_index(ti) * KCB, (uint32_t)KCB);
 #pragma unroll
         for (int mb = 0; mb < TILE / 16; ++mb) {
-            const uint8_t* p = kc + (size_t)(16 * mb + mrow) * KROW + mgrp * (KROW / 4);
+            const int so = 16 * mb * KROW;
             if constexpr (KW >= 4) {
 #pragma unroll
                 for (int w = 0; w < KW; w += 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(p + 4 * w);
+                    const uint4 v = buf_load16(r, kvo + 4 * w, so);
                     kw[mb][w] = v.x; kw[mb][w + 1] = v.y; kw[mb][w + 2] = v.z; kw[mb][w + 3] = v.w;
                 }
             } else if constexpr (KW == 2) {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                const uint2 v = buf_load8(r, kvo, so);
                 kw[mb][0] = v.x; kw[mb][1] = v.y;
             } else {
-                kw[mb][0] = *reinterpret_cast<const uint32_t*>(p);
+                kw[mb][0] = buf_load4(r, kvo, so);
             }
         }
     };
     auto load_v = [&](int ti) {
-        const uint8_t* vc = a.vc + tile_index(ti) * VCB;
+        const auto r = make_rsrc(a.vc + tile_index(ti) * VCB, (uint32_t)VCB);
 #pragma unroll
         for (int nb = 0; nb < NKB; ++nb) {
-            const uint8_t* p = vc + (size_t)(16 * nb + mrow) * VROW + mgrp * (VROW / 4);
+            const int so = 16 * nb * VROW;
             if constexpr (VW == 4) {
-                const uint4 v = *reinterpret_cast<const uint4*>(p);
+                const uint4 v = buf_load16(r, vvo, so);
                 vw[nb][0] = v.x; vw[nb][1] = v.y; vw[nb][2] = v.z; vw[nb][3] = v.w;
             } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                const uint2 v = buf_load8(r, vvo, so);
                 vw[nb][0] = v.x; vw[nb][1] = v.y;
             }
         }
@@ -336,6 +372,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             mt[r] = *src;
         }
     };
+    CodeMagic<KB> kmagic;
+    CodeMagic<VB> vmagic;
+    kmagic.init();
+    vmagic.init();
     load_meta(t0);
     load_k(t0);
     load_v(t0);
@@ -388,18 +428,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             }
         }
         wave_sync();
-        // MFMA B operand: q' rows n < G, zero rows above
+        // MFMA B operand: q' of head mrow; columns past the group repeat
+        // head G - 1 and their scores are never stored
         h4_t bq_hi[NKB], bq_lo[NKB];
         {
             const int row = mrow < G ? mrow : G - 1;
-            const h4_t z = {0, 0, 0, 0};
 #pragma unroll
             for (int k = 0; k < NKB; ++k) {
                 const int off = ((mgrp * G + row) * NKB + k) * 8;
-                const h4_t hi = *reinterpret_cast<const h4_t*>(bqimg + off);
-                const h4_t lo = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
-                bq_hi[k] = mrow < G ? hi : z;
-                bq_lo[k] = mrow < G ? lo : z;
+                bq_hi[k] = *reinterpret_cast<const h4_t*>(bqimg + off);
+                bq_lo[k] = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
             }
         }
 
@@ -409,7 +447,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int k = 0; k < NKB; ++k) {
-                const h4_t av = code_operand<KB, KW>(kw[mb], k);
+                const h4_t av = code_operand<KB, KW>(kw[mb], k, kmagic);
                 c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_hi[k], c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_lo[k], c, 0, 0, 0);
             }
@@ -477,18 +515,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             }
         }
         wave_sync();
-        // MFMA A operand: p' rows n < G, zero rows above
+        // MFMA A operand: p' of head mrow; rows past the group repeat head
+        // G - 1 and only rows of real heads are read back
         h4_t pa_hi[NVB], pa_lo[NVB];
         {
             const int row = mrow < G ? mrow : G - 1;
-            const h4_t z = {0, 0, 0, 0};
 #pragma unroll
             for (int k = 0; k < NVB; ++k) {
                 const int off = ((mgrp * G + row) * NVB + k) * 8;
-                const h4_t hi = *reinterpret_cast<const h4_t*>(paimg + off);
-                const h4_t lo = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
-                pa_hi[k] = mrow < G ? hi : z;
-                pa_lo[k] = mrow < G ? lo : z;
+                pa_hi[k] = *reinterpret_cast<const h4_t*>(paimg + off);
+                pa_lo[k] = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
             }
         }
 
@@ -498,7 +534,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int k = 0; k < NVB; ++k) {
-                const h4_t bv = code_operand<VB, VW>(vw[nb], k);
+                const h4_t bv = code_operand<VB, VW>(vw[nb], k, vmagic);
                 c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_hi[k], bv, c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_lo[k], bv, c, 0, 0, 0);
             }

@@ -34,6 +34,7 @@
 // number of younger loads.  A combine kernel merges the splits.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
+#include "kvarn_rsrc.hpp"
 
 namespace kvarn {
 
@@ -43,9 +44,6 @@ typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFp16TargetWaves = 8192;
-// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
-// format, no swizzle): byte offsets checked against num_records.
-constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2eF = 1.4426950408889634f;
 
 template <int D>
@@ -118,10 +116,8 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     // the step and block move only the scalar offset.
     const int rowb = 2 * d0;
     const uint32_t nrec = (uint32_t)(T * rowb);
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.k + (size_t)bg * T * d0), (short)0, (int)nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.v + (size_t)bg * T * d0), (short)0, (int)nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (size_t)bg * T * d0, nrec);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + (size_t)bg * T * d0, nrec);
     // K: token 16 mb + mrow, chunk c at byte 16 (4 c + mgrp) of the row
     const int kvo = mrow * rowb + 16 * mgrp;
     // V: token 16 kb + 4 mgrp + e, channels VCPL * mrow ..
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
             const int so = (int)((st * TS + 16 * mb) * rowb);
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
-                kr[mb][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + 64 * c, so, 0));
+                kr[mb][c] = buf_load16(krs, kvo + 64 * c, so);
         }
     };
     auto load_v = [&](int64_t st) {
@@ -146,13 +142,13 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
             for (int e = 0; e < 4; ++e) {
                 const int so = (int)((st * TS + 16 * kb2 + e) * rowb);
                 if constexpr (VCPL == 4) {
-                    const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, vvo, so, 0));
+                    const uint2 w = buf_load8(vrs, vvo, so);
                     vr[kb2][e][0] = w.x;
                     vr[kb2][e][1] = w.y;
                 } else {
 #pragma unroll
                     for (int u = 0; u < VCPL / 8; ++u) {
-                        const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vvo + 16 * u, so, 0));
+                        const uint4 w = buf_load16(vrs, vvo + 16 * u, so);
                         vr[kb2][e][4 * u + 0] = w.x;
                         vr[kb2][e][4 * u + 1] = w.y;
                         vr[kb2][e][4 * u + 2] = w.z;
