@@ -16,7 +16,9 @@
 // Centring the codes keeps both terms of each sum small (ZK is the group
 // minimum, so the uncentred terms would be large and of opposite sign).
 //
-// Matrix cores.  Both contractions run on v_mfma_f32_16x16x16_f16:
+// Matrix cores.  Both contractions run on v_mfma_f32_16x16x32_f16 (two
+// 16-deep operands side by side); the layouts below are those of the 16-deep
+// operands:
 //   q.K^T : A = codes (16 tokens x 16 channels), B = q' (16 channels x the
 //           GQA group's query heads, padded to 16), C = scores;
 //   p.V   : A = p' (query heads x 16 tokens), B = codes (16 tokens x 16
@@ -43,6 +45,7 @@ namespace kvarn {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTargetWaves = 8192;   // splits in flight: 8 waves per SIMD on 256 CUs
@@ -136,6 +139,14 @@ __device__ __forceinline__ h4_t code_operand(const uint32_t (&w)[NW], int kb, co
     const uint32_t lo = code_pair<B>(w[d], wh, 2 * k2, cm);
     const uint32_t hi = code_pair<B>(w[d], wh, 2 * k2 + 1, cm);
     return __builtin_bit_cast(h4_t, make_uint2(lo, hi));
+}
+
+// Two 16-deep operands side by side as one 32-deep operand of
+// v_mfma_f32_16x16x32_f16.  A and B pair their elements by (lane group,
+// element) alike, so concatenating operands 2j and 2j + 1 on both sides sums
+// exactly the products the two 16-deep instructions summed.
+__device__ __forceinline__ h8_t cat8(h4_t x, h4_t y) {
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Runs of a dense task that covers operands kbase, kbase + 1 (kbase even) of a
@@ -446,10 +457,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         for (int mb = 0; mb < TILE / 16; ++mb) {
             f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < NKB; ++k) {
-                const h4_t av = code_operand<KB, KW>(kw[mb], k, kmagic);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_hi[k], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bq_lo[k], c, 0, 0, 0);
+            for (int k = 0; k < NKB; k += 2) {
+                const h8_t av = cat8(code_operand<KB, KW>(kw[mb], k, kmagic),
+                                     code_operand<KB, KW>(kw[mb], k + 1, kmagic));
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cat8(bq_hi[k], bq_hi[k + 1]), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cat8(bq_lo[k], bq_lo[k + 1]), c, 0, 0, 0);
             }
             if (mrow < G)
                 *reinterpret_cast<f4_t*>(sc + mrow * TILE + 16 * mb + 4 * mgrp) = c;
@@ -533,10 +545,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         for (int nb = 0; nb < NKB; ++nb) {
             f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < NVB; ++k) {
-                const h4_t bv = code_operand<VB, VW>(vw[nb], k, vmagic);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_hi[k], bv, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_lo[k], bv, c, 0, 0, 0);
+            for (int k = 0; k < NVB; k += 2) {
+                const h8_t bv = cat8(code_operand<VB, VW>(vw[nb], k, vmagic),
+                                     code_operand<VB, VW>(vw[nb], k + 1, vmagic));
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(pa_hi[k], pa_hi[k + 1]), bv, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(pa_lo[k], pa_lo[k + 1]), bv, c, 0, 0, 0);
             }
             if (4 * mgrp < G)
                 *reinterpret_cast<f4_t*>(pvc + (16 * nb + mrow) * GP + 4 * mgrp) = c;
