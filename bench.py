@@ -243,8 +243,8 @@ def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seqs", type=int, default=LAYERS * KV_HEADS,
                     help="(layer, head) sequences in the CPU-oracle sample; 0 skips it")
     ap.add_argument("--no-paged", action="store_true",
