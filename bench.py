@@ -202,6 +202,55 @@ def paged_attention_measure(kv, kc, vc, km, vm, q, reps=20):
                         "tokens), GQA 32/8, K4V2; outside the timed step"}
 
 
+def stream_reference(dev, units, reps=5):
+    """Plain streaming kernels moving each stage's bytes per tile pair
+    (libkvarn_streamref.so, built with the library): the rate this device
+    delivers for that read/write mix, the reference for each stage's HBM
+    fraction beside the nominal 8 TB/s.  Best of three persistent grid sizes."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_bit_token_amd", "libkvarn_streamref.so"))
+    fn = lib.kvarn_stream_reference
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    b = per_tile_bytes(HEAD_DIM)
+    big, small = b["fp16_pair"] // 16, b["packed_pair"] // 16
+    src = torch.empty(units * big * 16, dtype=torch.uint8, device=dev)
+    dst = torch.empty(units * big * 16, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    mixes = {"quantize_mix": (big, small), "dequantize_mix": (small, big),
+             "packed_read": (small, 0), "fp16_read": (big, 0)}
+    out = {}
+    for name, (rq, wq) in mixes.items():
+        best = None
+        for per_cu in (4, 8, 16):
+            def run():
+                st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, sink.data_ptr(), stream)
+                if st != 0:
+                    raise RuntimeError("stream reference launch failed: %d" % st)
+            for _ in range(2):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            best = ms if best is None else min(best, ms)
+        nbytes = units * (rq + wq) * 16
+        out[name] = {"ms": round(best, 4), "GBps": round(nbytes / (best / 1e3) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (best / 1e3) / HBM_PEAK, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
     """Decode attention over the uncompressed fp16 cache of the same workload
     (the baseline of the pages' throughput comparison), timed with HIP events
@@ -251,6 +300,8 @@ def main():
                     help="skip the paged-cache decode-attention measurement")
     ap.add_argument("--no-fp16", action="store_true",
                     help="skip the fp16-cache decode-attention baseline")
+    ap.add_argument("--no-stream-ref", action="store_true",
+                    help="skip the streaming reference kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -360,9 +411,18 @@ def main():
                      "hbm_frac": stages["quantize"]["hbm_frac"]},
         "wall_s": round(t_wall, 3),
     }
+    if not args.no_stream_ref:
+        ref = stream_reference(dev, n_tiles)
+        result["stream_reference"] = ref
+        for stage, mix in (("quantize", "quantize_mix"), ("dequantize", "dequantize_mix"),
+                           ("decode_attention", "packed_read")):
+            stages[stage]["achievable_frac"] = round(stages[stage]["hbm_GBps"] / ref[mix]["GBps"], 4)
     if not args.no_fp16:
         result["fp16_decode_attention"] = fp16_attention_measure(
             kv, k, v, q, out, stages["decode_attention"]["ms"])
+        if "stream_reference" in result:
+            f = result["fp16_decode_attention"]
+            f["achievable_frac"] = round(f["hbm_GBps"] / result["stream_reference"]["fp16_read"]["GBps"], 4)
     if not args.no_paged:
         result["paged_decode_attention"] = paged_attention_measure(kv, kc, vc, km, vm, q)
     if args.cpu_seqs > 0:

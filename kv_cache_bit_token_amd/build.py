@@ -14,6 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvarn.so")
+# streaming reference kernels for bench.py only (not part of the library's ABI)
+STREAM_SRC = "bench_stream.hip"
+STREAM_LIB = os.path.join(HERE, "libkvarn_streamref.so")
 SOURCES = ["kvarn_abi.cpp", "kvarn_quantize.hip", "kvarn_dequantize.hip", "kvarn_attention.hip",
            "kvarn_attention_fp16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,15 +44,21 @@ def _compile(src: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+def _link(objs, lib, verbose):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + [STREAM_SRC]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], STREAM_LIB, verbose)
     return LIB
 
 
