@@ -206,7 +206,8 @@ def stream_reference(dev, units, reps=5):
     """Plain streaming kernels moving each stage's bytes per tile pair
     (libkvarn_streamref.so, built with the library): the rate this device
     delivers for that read/write mix, the reference for each stage's HBM
-    fraction beside the nominal 8 TB/s.  Best of three persistent grid sizes."""
+    fraction beside the nominal 8 TB/s.  Best of a loop kernel and an
+    unrolled one, each at three persistent grid sizes."""
     import ctypes
     import torch
 
@@ -214,7 +215,7 @@ def stream_reference(dev, units, reps=5):
     fn = lib.kvarn_stream_reference
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     b = per_tile_bytes(HEAD_DIM)
     big, small = b["fp16_pair"] // 16, b["packed_pair"] // 16
     src = torch.empty(units * big * 16, dtype=torch.uint8, device=dev)
@@ -227,9 +228,10 @@ def stream_reference(dev, units, reps=5):
     out = {}
     for name, (rq, wq) in mixes.items():
         best = None
-        for per_cu in (4, 8, 16):
+        for per_cu, unrolled in ((4, 0), (8, 0), (16, 0), (4, 1), (8, 1), (16, 1)):
             def run():
-                st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, sink.data_ptr(), stream)
+                st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, unrolled,
+                        sink.data_ptr(), stream)
                 if st != 0:
                     raise RuntimeError("stream reference launch failed: %d" % st)
             for _ in range(2):
