@@ -291,6 +291,93 @@ def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
                         "outside the timed step"}
 
 
+def config_sweep(kv, synthetic, dev, reps=10):
+    """The other workloads, timed kernel by kernel with HIP events (inputs
+    resident; small working sets rotated across copies totalling > 512 MB so
+    the 256 MB last-level cache cannot hold them):
+      dequantize         256 seq x 8 KV heads x 8192 tokens x 128 (packed by the quantiser)
+      head_dim sweep     8 KV heads x 32768 tokens, head_dim 64 / 96 / 256, 3 and 5 iterations
+      decode attention   64 seq x 8 KV heads x 32768 tokens, GQA 32/8, and its fp16 baseline
+    """
+    import torch
+
+    def timed(fns):
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fns[i % len(fns)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def rates(ms, fp16_bytes, hbm_bytes, pairs):
+        return {"ms": round(ms, 4), "fp16_equiv_GBps": round(fp16_bytes / (ms / 1e3) / 1e9, 1),
+                "hbm_GBps": round(hbm_bytes / (ms / 1e3) / 1e9, 1),
+                "hbm_frac": round(hbm_bytes / (ms / 1e3) / HBM_PEAK, 4),
+                "tile_pairs_per_s": round(pairs / (ms / 1e3), 0)}
+
+    out = {}
+    # dequantize, 256 x 8 x 8192
+    k, v = synthetic.outlier_kv_torch(1, 256 * 8, 8192, 128, dev)
+    kt, vt = k.view(-1, 128, 128), v.view(-1, 128, 128)
+    packed = kv.quantize_tiles(kt, vt)
+    n = kt.shape[0]
+    b = per_tile_bytes(128)
+    ms = timed([lambda: kv.dequantize_tiles(*packed, head_dim=128, out=(kt, vt))])
+    out["dequantize_256x8x8192"] = rates(ms, n * b["fp16_pair"], n * (b["fp16_pair"] + b["packed_pair"]), n)
+    del k, v, kt, vt, packed
+    torch.cuda.empty_cache()
+    # head_dim sweep
+    for d0 in (64, 96, 256):
+        D = 64 if d0 <= 64 else (128 if d0 <= 128 else 256)
+        k, v = synthetic.outlier_kv_torch(4, 8, 32768, d0, dev)
+        kt, vt = k.view(-1, 128, d0), v.view(-1, 128, d0)
+        n = kt.shape[0]
+        fp16 = 2 * n * 128 * d0 * 2
+        copies = max(2, -(-(512 << 20) // fp16) + 1)
+        ins = [(kt.clone(), vt.clone()) for _ in range(copies)]
+        lay = kv.get_layout(d0, 4, 2, 5)
+        packed_b = n * (lay["k_code_bytes"] + lay["v_code_bytes"] + lay["k_meta_bytes"] + lay["v_meta_bytes"])
+        for it in (3, 5):
+            outs = [kv.quantize_tiles(a, c, n_iters=it) for a, c in ins]
+            ms_q = timed([lambda a=a, c=c, o=o: kv.quantize_tiles(a, c, n_iters=it, out=o)
+                          for (a, c), o in zip(ins, outs)])
+            ms_d = timed([lambda a=a, c=c, o=o: kv.dequantize_tiles(*o, head_dim=d0, out=(a, c))
+                          for (a, c), o in zip(ins, outs)])
+            key = "head_dim_%d_iters_%d" % (d0, it)
+            out[key] = {"padded": D, "quantize": rates(ms_q, fp16, fp16 + packed_b, n),
+                        "dequantize": rates(ms_d, fp16, fp16 + packed_b, n)}
+            del outs
+        del k, v, kt, vt, ins
+        torch.cuda.empty_cache()
+    # decode attention, 64 x 8 x 32768, and the fp16 baseline
+    k, v = synthetic.outlier_kv_torch(5, 64 * 8, 32768, 128, dev)
+    kt, vt = k.view(-1, 128, 128), v.view(-1, 128, 128)
+    kc, vc, km, vm = kv.quantize_tiles(kt, vt)
+    q = synthetic.query_torch(5, 64, 32, 128, dev)
+    n = kt.shape[0]
+    wsb = kv.decode_attention_workspace(batch=64, n_q_heads=32, n_kv_heads=8, tiles_per_seq=256,
+                                        head_dim=128)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((64, 32, 128), dtype=torch.float32, device=dev)
+    ms = timed([lambda: kv.decode_attention(q, kc, vc, km, vm, n_kv_heads=8, tiles_per_seq=256,
+                                            workspace=ws, out=o)])
+    out["decode_attention_64x8x32768"] = rates(ms, n * b["fp16_pair"], n * b["packed_pair"], n)
+    k4, v4 = k.view(64, 8, 32768, 128), v.view(64, 8, 32768, 128)
+    wsf = torch.empty(max(kv.decode_attention_fp16_workspace(batch=64, n_q_heads=32, n_kv_heads=8,
+                                                             seq_len=32768, head_dim=128), 16),
+                      dtype=torch.uint8, device=dev)
+    ms_f = timed([lambda: kv.decode_attention_fp16(q, k4, v4, workspace=wsf, out=o)])
+    out["fp16_decode_attention_64x8x32768"] = rates(ms_f, n * b["fp16_pair"], n * b["fp16_pair"], n)
+    out["fp16_decode_attention_64x8x32768"]["packed_speedup"] = round(ms_f / ms, 3)
+    del k, v, kt, vt, kc, vc, km, vm, k4, v4
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +391,9 @@ def main():
                     help="skip the fp16-cache decode-attention baseline")
     ap.add_argument("--no-stream-ref", action="store_true",
                     help="skip the streaming reference kernels")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the other workloads kernel by kernel (dequantize 256x8x8192, "
+                         "head_dim sweep, attention 64x8x32768)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -427,6 +517,10 @@ def main():
             f["achievable_frac"] = round(f["hbm_GBps"] / result["stream_reference"]["fp16_read"]["GBps"], 4)
     if not args.no_paged:
         result["paged_decode_attention"] = paged_attention_measure(kv, kc, vc, km, vm, q)
+    if args.configs:
+        del ko, vo
+        torch.cuda.empty_cache()
+        result["other_workloads"] = config_sweep(kv, synthetic, dev)
     if args.cpu_seqs > 0:
         result["cpu_baseline"] = cpu_baseline(k, v, q, args.cpu_seqs)
     print(json.dumps(result), flush=True)
