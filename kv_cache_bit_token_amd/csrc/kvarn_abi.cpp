@@ -183,7 +183,7 @@ kvarn_status kvarn_decode_attention_workspace(const kvarn_params* params, int32_
     if (st != KVARN_OK) return st;
     int ns = 0, tps = 0;
     kvarn::attention_plan(batch, n_kv_heads, tiles_per_seq, &ns, &tps);
-    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns);
+    *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
     return KVARN_OK;
 }
 
@@ -206,7 +206,7 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, int32_t batch, i
     int ns = 0, tps = 0;
     kvarn::attention_plan(batch, n_kv_heads, tiles_per_seq, &ns, &tps);
     if (tiles_per_seq > 0 &&
-        workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns))
+        workspace_bytes < kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns))
         return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
 
@@ -280,7 +280,7 @@ kvarn_status kvarn_decode_attention_paged_workspace(const kvarn_params* params, 
     int ns = 0, tps = 0;
     kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
     if (max_blocks == 0) ns = 0;
-    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
+    *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
     return KVARN_OK;
 }
 
@@ -313,7 +313,7 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t ba
     int ns = 0, tps = 0;
     kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
     if (max_blocks == 0) ns = 0;
-    if (workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
+    if (workspace_bytes < kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
         return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
 

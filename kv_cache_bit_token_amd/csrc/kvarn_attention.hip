@@ -71,6 +71,15 @@ size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
     return (size_t)batch * n_q_heads * n_parts * (D + 2) * sizeof(float);
 }
 
+// byte offset of the rotated queries: the partials rounded up to 256 bytes
+static size_t qrot_offset(int batch, int n_q_heads, int D, int n_parts) {
+    return (attention_workspace_bytes(batch, n_q_heads, D, n_parts) + 255) & ~(size_t)255;
+}
+
+size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
+    return qrot_offset(batch, n_q_heads, D, n_parts) + (size_t)batch * n_q_heads * D * sizeof(float);
+}
+
 // ---- b-bit codes -> exact fp16 (code - 2^(b-1)) -----------------------------
 // A packed dword holds N = 32/b codes.  Pair k takes codes k and k + N/2 (bits
 // b*k and b*k + 16) into the two halves of a dword.  A code sitting at bit s
@@ -206,6 +215,37 @@ struct AttnLds {
     __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * G + 16; }
 };
 
+template <int D>
+__device__ void lds_fwht(float* v, int rows) {
+    const int tid = threadIdx.x;
+    for (int h = 1; h < D; h <<= 1) {
+        for (int k = tid; k < rows * D / 2; k += blockDim.x) {
+            const int r = k / (D / 2), p = k % (D / 2);
+            const int lo = (p / h) * 2 * h + (p % h), hi = lo + h;
+            const float x = v[r * D + lo], y = v[r * D + hi];
+            v[r * D + lo] = x + y;
+            v[r * D + hi] = x - y;
+        }
+        __syncthreads();
+    }
+    const float s = 1.0f / __builtin_sqrtf((float)D);
+    for (int k = tid; k < rows * D; k += blockDim.x) v[k] *= s;
+    __syncthreads();
+}
+
+// Rotated query of one (b, query head): H q / sqrt(D) over the padded width,
+// once per head for every split that reads it.
+template <int D>
+__global__ __launch_bounds__(128) void attn_rotate_q_kernel(AttnArgs a) {
+    __shared__ float v[D];
+    const int bh = blockIdx.x;   // b * n_q_heads + h
+    for (int j = threadIdx.x; j < D; j += blockDim.x)
+        v[j] = (j < a.d0) ? h2f_bits(a.q[(size_t)bh * a.d0 + j]) : 0.0f;
+    __syncthreads();
+    lds_fwht<D>(v, 1);
+    for (int j = threadIdx.x; j < D; j += blockDim.x) a.qrot[(size_t)bh * D + j] = v[j];
+}
+
 template <int D, int KB, int VB, int GMAX>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     using L = AttnLds<D>;
@@ -265,55 +305,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
     const int mrow = lane & 15;     // MFMA row / column index of this lane
     const int mgrp = lane >> 4;     // MFMA k-group of this lane
-
-    // ---- rotated queries, held by the dense q'-build tasks ----
-    // task t: query n = t / QT; lane group gq = (t % QT) / (NKB / 2); pair pr
-    float qh[QTMAX][8];
-    {
-        float* tmp = sc;   // [G][D] scratch before the tile loop
-        for (int k = lane; k < G * D; k += 64) {
-            const int n = k / D, j = k % D;
-            const int h = g * G + n;
-            tmp[k] = (j < a.d0) ? h2f_bits(a.q[((size_t)b * a.n_q_heads + h) * a.d0 + j]) : 0.0f;
-        }
-        wave_sync();
-        // in-LDS Walsh-Hadamard transform of each query row
-        for (int hs = 1; hs < D; hs <<= 1) {
-            for (int k = lane; k < G * D / 2; k += 64) {
-                const int r = k / (D / 2), p = k % (D / 2);
-                const int lo = (p / hs) * 2 * hs + (p % hs), hi = lo + hs;
-                const float x = tmp[r * D + lo], y = tmp[r * D + hi];
-                tmp[r * D + lo] = x + y;
-                tmp[r * D + hi] = x - y;
-            }
-            wave_sync();
-        }
-        const float rs = 1.0f / __builtin_sqrtf((float)D);
-#pragma unroll
-        for (int r = 0; r < QTMAX; ++r) {
-            const int t = lane + 64 * r;
-            const int n = t / QT, rem = t % QT;
-            const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
-            const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qh[r][e] = (n < G) ? tmp[n * D + r0 + e] * rs : 0.0f;
-                qh[r][4 + e] = (n < G) ? tmp[n * D + r1 + e] * rs : 0.0f;
-            }
-        }
-        wave_sync();
-    }
-
-    // softmax state of the dense score tasks (task t: query t / 16)
-    float m_run[STMAX], l_run[STMAX];
-#pragma unroll
-    for (int r = 0; r < STMAX; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
-    // dense accumulator: channel lane + 64 * r, query n
-    float acc[CPL_E][GMAX];
-#pragma unroll
-    for (int r = 0; r < CPL_E; ++r)
-#pragma unroll
-        for (int n = 0; n < GMAX; ++n) acc[r][n] = 0.0f;
 
     // Loads run one tile ahead, each issued once its registers are free: the
     // next tile's meta right after this tile's meta is in LDS, its K codes
@@ -383,13 +374,44 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             mt[r] = *src;
         }
     };
+    // The group's rotated queries (H q / sqrt(D), from the rotation kernel)
+    // and then the first tile go out before anything waits.
+    // task t: query n = t / QT; lane group gq = (t % QT) / (NKB / 2); pair pr
+    float qh[QTMAX][8];
+#pragma unroll
+    for (int r = 0; r < QTMAX; ++r) {
+        const int t = lane + 64 * r;
+        const int n = t / QT, rem = t % QT;
+        const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
+        const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
+        const float* src = a.qrot + ((size_t)b * a.n_q_heads + g * G + (n < G ? n : G - 1)) * D;
+        const float4 lo = *reinterpret_cast<const float4*>(src + r0);
+        const float4 hi = *reinterpret_cast<const float4*>(src + r1);
+        const bool live = n < G;
+        qh[r][0] = live ? lo.x : 0.0f; qh[r][1] = live ? lo.y : 0.0f;
+        qh[r][2] = live ? lo.z : 0.0f; qh[r][3] = live ? lo.w : 0.0f;
+        qh[r][4] = live ? hi.x : 0.0f; qh[r][5] = live ? hi.y : 0.0f;
+        qh[r][6] = live ? hi.z : 0.0f; qh[r][7] = live ? hi.w : 0.0f;
+    }
+    load_meta(t0);
+    load_k(t0);
+    load_v(t0);
+
+    // softmax state of the dense score tasks (task t: query t / 16)
+    float m_run[STMAX], l_run[STMAX];
+#pragma unroll
+    for (int r = 0; r < STMAX; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
+    // dense accumulator: channel lane + 64 * r, query n
+    float acc[CPL_E][GMAX];
+#pragma unroll
+    for (int r = 0; r < CPL_E; ++r)
+#pragma unroll
+        for (int n = 0; n < GMAX; ++n) acc[r][n] = 0.0f;
+
     CodeMagic<KB> kmagic;
     CodeMagic<VB> vmagic;
     kmagic.init();
     vmagic.init();
-    load_meta(t0);
-    load_k(t0);
-    load_v(t0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile, once
 
     for (int ti = t0; ti < t1; ++ti) {
@@ -603,24 +625,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 }
 
 template <int D>
-__device__ void lds_fwht(float* v, int rows) {
-    const int tid = threadIdx.x;
-    for (int h = 1; h < D; h <<= 1) {
-        for (int k = tid; k < rows * D / 2; k += blockDim.x) {
-            const int r = k / (D / 2), p = k % (D / 2);
-            const int lo = (p / h) * 2 * h + (p % h), hi = lo + h;
-            const float x = v[r * D + lo], y = v[r * D + hi];
-            v[r * D + lo] = x + y;
-            v[r * D + hi] = x - y;
-        }
-        __syncthreads();
-    }
-    const float s = 1.0f / __builtin_sqrtf((float)D);
-    for (int k = tid; k < rows * D; k += blockDim.x) v[k] *= s;
-    __syncthreads();
-}
-
-template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     __shared__ float o[D];
     const int tid = threadIdx.x;
@@ -819,9 +823,17 @@ __global__ void fill_zero_kernel(float* out, int64_t n) {
 }
 
 template <int D, int KB, int VB, int GMAX>
-static hipError_t launch_att(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
+    AttnArgs a = args;
     const int G = a.n_q_heads / a.n_kv_heads;
     if (a.n_splits > 0) {
+        // the rotated queries follow the split partials in the workspace
+        a.qrot = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) +
+                                          qrot_offset(a.batch, a.n_q_heads, D, a.n_parts));
+        hipLaunchKernelGGL((attn_rotate_q_kernel<D>), dim3((unsigned)(a.batch * a.n_q_heads)), dim3(128),
+                           0, s, a);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
         const int per_wave = AttnLds<D>::bytes(G);
         int wpb = 65536 / per_wave;
         if (wpb > 4) wpb = 4;

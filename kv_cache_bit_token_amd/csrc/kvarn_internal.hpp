@@ -58,6 +58,7 @@ struct AttnArgs {
     const uint16_t* k_tail = nullptr;   // [batch][n_kv_heads][128][d0]
     const uint16_t* v_tail = nullptr;
     int64_t pool_blocks = 0;
+    float* qrot = nullptr;              // [B][Hq][D] rotated queries (set by the launcher)
 };
 
 // Decode attention over an uncompressed fp16 cache (the baseline).
@@ -86,6 +87,8 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_
 void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
                     int* tiles_per_split);
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
+// Packed-cache attention: the split partials, then the rotated queries.
+size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 
 // Split plan of the fp16-cache attention (token steps of 32 * 128 / D).
 void attention_fp16_plan(int batch, int n_kv_heads, int64_t seq_len, int D, int* n_splits,
