@@ -2,7 +2,7 @@
 // cache, gfx950: the baseline that the packed cache is measured against.
 //
 // Pages: hotdry page "KVarN Hadamard 旋转与方差归一化", section on the
-// deployment parameters (throughput is judged against an FP16 baseline);
+// deployment parameters (throughput is compared with an FP16 baseline);
 // deep page, section "一次 16K context 的推論，記憶體都花到哪去了" (every
 // decode step reads the whole cache from HBM, so decode is bound by memory
 // bandwidth and a smaller cache makes it faster).

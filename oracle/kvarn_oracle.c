@@ -22,7 +22,7 @@
  * compared against this file: the double value u is rounded to float and
  * then to the nearest integer (ties to even).
  *
- * Readings of points the pages leave open (each one is listed in the design doc):
+ * Readings of points the pages leave open:
  *   - A tile is 128 tokens x D channels; the rotation runs along channels
  *     (head_dim) for K and for V ([hotdry] §Hadamard 旋转; [deep] stage card
  *     "Hadamard rotation").
