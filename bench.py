@@ -125,8 +125,35 @@ def cpu_baseline(k, v, q, n_seq, chunk=32):
         del qk, qv, kt, vt
     n_tiles = n_seq * tiles_per_seq
     fp16_bytes = 3 * n_tiles * per_tile_bytes(HEAD_DIM)["fp16_pair"]
+    # one thread, on the first 512 tokens of the first (layer, head): the same
+    # three stages over its 4 tile pairs
+    oracle.set_threads(1)
+    kt = kt_all[:4].cpu().numpy()
+    vt = vt_all[:4].cpu().numpy()
+    qh = q[0:1, 0:Q_HEADS // KV_HEADS].cpu().numpy()
+    t0 = time.perf_counter()
+    qk = oracle.quantize_tiles(kt, K_BITS, N_ITERS, True)
+    qv = oracle.quantize_tiles(vt, V_BITS, N_ITERS, False)
+    oracle.dequantize_tiles(qk["codes"], qk["meta"], HEAD_DIM, K_BITS, True)
+    oracle.dequantize_tiles(qv["codes"], qv["meta"], HEAD_DIM, V_BITS, False)
+    oracle.decode_attention(qh, qk["codes"], qv["codes"], qk["meta"], qv["meta"], n_kv_heads=1,
+                            tiles_per_seq=4, k_bits=K_BITS, v_bits=V_BITS)
+    dt1 = time.perf_counter() - t0
+    oracle.set_threads(threads)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(fp16_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "cpu_model": model,
+            "single_thread": {"value": round(3 * 4 * per_tile_bytes(HEAD_DIM)["fp16_pair"] / dt1 / 1e9, 4),
+                              "unit": "GB/s", "seconds": round(dt1, 4),
+                              "sample": "first 512 tokens of the first (layer, head), 4 tile pairs"},
             "sample": "%d of %d (layer, head) sequences (%d tile pairs): quantize + dequantize "
                       "+ decode attention of their query heads, fp64 oracle, same inputs and unit "
                       "as value" % (n_seq, LAYERS * KV_HEADS, n_tiles)}
