@@ -34,8 +34,9 @@ int pointer_set(const void* a, const void* b, const void* c) {
 
 int64_t code_bytes(int D, int bits) { return (int64_t)TILE * D * bits / 8; }
 
-// Largest tile count one launch grid can hold (K and V share the grid).
-constexpr int64_t kMaxTiles = (int64_t)1 << 30;
+// Largest tile count one launch grid can hold (K and V share the grid, whose
+// x dimension holds at most 2^31 - 1 workgroups).
+constexpr int64_t kMaxTiles = ((int64_t)1 << 30) - 1;
 
 }  // namespace
 
@@ -168,6 +169,7 @@ static kvarn_status check_attention_shape(int32_t batch, int32_t n_q_heads, int3
         return KVARN_E_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return KVARN_E_SHAPE;
     if (n_q_heads / n_kv_heads > 16) return KVARN_E_SHAPE;   // GQA group of at most 16 heads
+    if ((int64_t)batch * n_q_heads > INT32_MAX) return KVARN_E_SHAPE;   // one workgroup per (b, head)
     if ((int64_t)batch * n_kv_heads * tiles_per_seq > kMaxTiles) return KVARN_E_SHAPE;
     return KVARN_OK;
 }
