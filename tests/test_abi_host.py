@@ -238,3 +238,18 @@ def test_python_api_refuses_cpu_tensors(name):
             t = torch.zeros(1, 1, 128, 128, dtype=torch.float16)
             kv.decode_attention_paged(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m, i,
                                       i[0], i[0], t, t, n_kv_heads=1)
+
+
+def test_grid_bounds_refused_on_the_host():
+    """Counts that would not fit one launch grid come back as KVARN_E_SHAPE."""
+    lib = _lib.load()
+    ok = ctypes.byref(P())
+    q = lib.kvarn_quantize_tiles
+    assert q(ok, 1 << 30, A, A, A, A, A, A, None) == 6            # 2^30 tiles of K and of V
+    assert q(ok, (1 << 30) - 1, None, None, None, None, None, None, None) == 0   # skipped: no launch
+    nb = ctypes.c_size_t()
+    ws = lib.kvarn_decode_attention_workspace
+    assert ws(ok, 1 << 27, 32, 8, 0, ctypes.byref(nb)) == 6         # 2^32 (b, head) pairs
+    assert ws(ok, 1 << 20, 32, 8, 1 << 10, ctypes.byref(nb)) == 6   # 2^33 tiles
+    fws = lib.kvarn_decode_attention_fp16_workspace
+    assert fws(128, 1 << 27, 32, 8, 128, ctypes.byref(nb)) == 6
