@@ -259,6 +259,11 @@ __device__ __forceinline__ float h2f_bits(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// value of lane L (wave-uniform result)
+__device__ __forceinline__ float lane_f(float v, int L) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), L));
+}
+
 // Orders the LDS accesses of one wavefront: what its lanes wrote before is
 // visible to its lanes after (no workgroup barrier).
 __device__ __forceinline__ void wave_sync() {

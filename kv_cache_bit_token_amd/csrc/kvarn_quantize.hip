@@ -102,9 +102,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     fwht_crosslane<R>(x, cb);
 
     // ---------------- normalisation ----------------
-    float a[TPL], Rt[TPL];          // 1 / R[t] and R[t] = exp(l_r[t]) for my tokens
+    // Only the reciprocal factors are carried through the iterations:
+    // R[t] = exp(l_r[t]) = 1 / a[t] and C = 1 / Cinv are formed once at the end.
+    float a[TPL];                   // 1 / R[t] for my tokens
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) { a[i] = 1.0f; Rt[i] = 1.0f; }
+    for (int i = 0; i < TPL; ++i) a[i] = 1.0f;
     float b[CPL];                   // 1 / C[c] for my channels (unscaled units)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) b[c] = rsqrtD;
@@ -113,17 +115,18 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     const int rp = tid >> 1, rh = tid & 1;
     const float2* rpart = part + PST * (16 * rh + (rp >> 4)) + (rp & 15);
     float2* wpart = part + PST * tid;
-    float Cp = sqrtD;   // column factor of position rp, unscaled units (exp(l_c) * sqrt(D))
-    float Cinv = rsqrtD;
+    float Cinv = rsqrtD;   // 1 / column factor of position rp, unscaled units (exp(-l_c) / sqrt(D))
     if (tid == 0) *flag = 0;
 
     for (int it = 0; it < n_iters; ++it) {
         // ---- column pass: raw moments over tokens of x * a ----
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            float s1 = 0.0f, s2 = 0.0f;
+            // the sums start from the first term, not from 0 (no add of 0)
+            const float v0 = x[0][c] * a[0];
+            float s1 = v0, s2 = v0 * v0;
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) {
+            for (int i = 1; i < TPL; ++i) {
                 const float v = x[i][c] * a[i];
                 s1 += v;
                 s2 = __builtin_fmaf(v, v, s2);
@@ -131,26 +134,28 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             wpart[c] = make_float2(s1, s2);
         }
         __syncthreads();
-        const float Cprev = Cp;
+        const float Cinv_prev = Cinv;
         float cmean;
         {
-            float s1 = 0.0f, s2 = 0.0f;
+            float s1 = rpart[0].x, s2 = rpart[0].y;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 1; k < 16; ++k) {
                 const float2 v = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
                 s1 += v.x;
                 s2 += v.y;
             }
             s1 += dpp<DPP_XOR1>(s1);
             s2 += dpp<DPP_XOR1>(s2);
-            cmean = s1 * (1.0f / TILE);
-            const float var = __builtin_fmaf(-cmean, cmean, s2 * (1.0f / TILE));
+            // m2 = 2 mean, so t = 4 mean^2 serves both the variance and the test
+            const float m2 = s1 * (2.0f / TILE);
+            const float t = m2 * m2;
+            cmean = 0.5f * m2;
+            const float var = __builtin_fmaf(t, -0.25f, s2 * (1.0f / TILE));
             // accurate unless the mean dominates the spread (4 mean^2 >= var,
             // which also covers var <= 0)
-            const bool ok = 4.0f * cmean * cmean < var;
+            const bool ok = t < var;
             const float ci = __builtin_amdgcn_rsqf(var);
             Cinv = ok ? ci : Cinv;
-            Cp = ok ? var * ci : Cp;
             if (!ok) *flag = 1;
             if (rh == 0) colv[rp] = Cinv;
         }
@@ -181,8 +186,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
                 for (int k = 0; k < 16; ++k) q += rpart[PST * R * (k % DL + (k / DL) * 2 * DL)].x;
                 q += dpp<DPP_XOR1>(q);
                 const float sd = __builtin_sqrtf(q * (1.0f / TILE));
-                Cp = is_flat(sd, cmean) ? Cprev : sd;
-                Cinv = 1.0f / Cp;
+                Cinv = is_flat(sd, cmean) ? Cinv_prev : 1.0f / sd;
                 if (rh == 0) colv[rp] = Cinv;
             }
             __syncthreads();
@@ -194,20 +198,22 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         if (!IS_K && it == n_iters - 1) break;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            float s1 = 0.0f, s2 = 0.0f;
+            const float v0 = x[i][0] * b[0];
+            float s1 = v0, s2 = v0 * v0;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
+            for (int c = 1; c < CPL; ++c) {
                 const float v = x[i][c] * b[c];
                 s1 += v;
                 s2 = __builtin_fmaf(v, v, s2);
             }
             s1 = rg_sum<R>(s1);
             s2 = rg_sum<R>(s2);
-            const float mean = s1 * (1.0f / D);
-            const float var = __builtin_fmaf(-mean, mean, s2 * (1.0f / D));
+            const float m2 = s1 * (2.0f / D);   // 2 mean
+            const float t = m2 * m2;            // 4 mean^2
+            const float var = __builtin_fmaf(t, -0.25f, s2 * (1.0f / D));
             float ai = __builtin_amdgcn_rsqf(var);
-            float ri = var * ai;
-            if (!(4.0f * mean * mean < var)) {
+            if (!(t < var)) {
+                const float mean = 0.5f * m2;
                 // fallback for this token (uniform across its row-group)
                 float q = 0.0f;
 #pragma unroll
@@ -216,11 +222,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
                     q = __builtin_fmaf(d, d, q);
                 }
                 const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
-                ri = is_flat(sd, mean) ? Rt[i] : sd;
-                ai = 1.0f / ri;
+                ai = is_flat(sd, mean) ? a[i] : 1.0f / sd;
             }
             a[i] = ai;
-            Rt[i] = ri;
         }
     }
 
@@ -230,19 +234,22 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     // column factors) so the stored fp16 factors stay in range even when the
     // iteration drifts the two sets apart.  Codes are unaffected; only the
     // stored SK/ZK/RK (K) and SV/ZV/CV (V) see G.
+    // Base-2 logarithms and powers on the hardware units: G only moves the
+    // stored factors, so its own last-place error never reaches a code.
     float G, invG;
     {
-        float s = logf(Cp * rsqrtD);   // both lanes of a position: the sum is 2x
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        // log2 of the column factor; both lanes of a position: the sum is 2x
+        float s = -__builtin_amdgcn_logf(Cinv * sqrtD);
+        s = rg_sum<16>(s);   // sum over each 16-lane DPP row
+        s = lane_f(s, 0) + lane_f(s, 16) + lane_f(s, 32) + lane_f(s, 48);
         if ((tid & 63) == 0) gsum[tid >> 6] = s;
         __syncthreads();
-        float tot = 0.0f;
+        float tot = gsum[0];
 #pragma unroll
-        for (int w = 0; w < NT / 64; ++w) tot += gsum[w];
-        const float mean_lc = tot * (0.5f / D);
-        G = expf(mean_lc);
-        invG = expf(-mean_lc);
+        for (int w = 1; w < NT / 64; ++w) tot += gsum[w];
+        const float mean_l2 = tot * (0.5f / D);
+        G = __builtin_amdgcn_exp2f(mean_l2);
+        invG = __builtin_amdgcn_exp2f(-mean_l2);
     }
     // Sylvester channel index of the reducer's lane position
     const int kpos = 16 * N::nu(rp >> 4) + (rp & 15);
@@ -287,8 +294,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         }
         __syncthreads();
         if (cb == 0) {   // RK of my 4 tokens
-            const uint32_t lo = f2h_bits(Rt[0] * G) | ((uint32_t)f2h_bits(Rt[1] * G) << 16);
-            const uint32_t hi = f2h_bits(Rt[2] * G) | ((uint32_t)f2h_bits(Rt[3] * G) << 16);
+            float rk[TPL];   // R[t] G
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) rk[i] = G * __builtin_amdgcn_rcpf(a[i]);
+            const uint32_t lo = f2h_bits(rk[0]) | ((uint32_t)f2h_bits(rk[1]) << 16);
+            const uint32_t hi = f2h_bits(rk[2]) | ((uint32_t)f2h_bits(rk[3]) << 16);
             *reinterpret_cast<uint2*>(meta_out + 2 * D + 4 * tb) = make_uint2(lo, hi);
         }
         float inv[CPL], off[CPL];
@@ -349,7 +359,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             *reinterpret_cast<uint2*>(meta_out + 4 * tb) = make_uint2(sv2[0], sv2[1]);
             *reinterpret_cast<uint2*>(meta_out + TILE + 4 * tb) = make_uint2(zv2[0], zv2[1]);
         }
-        if (rh == 0) meta_out[2 * TILE + kpos] = f2h_bits(Cp * rsqrtD * invG);   // CV
+        if (rh == 0) meta_out[2 * TILE + kpos] = f2h_bits(invG * rsqrtD * __builtin_amdgcn_rcpf(Cinv));   // CV
 
         // Channel-major stream: channel k's codes of tokens 4*tb .. +3 form
         // BITS/2 bytes at k * (TILE * BITS / 8) + (BITS / 2) * tb.  Each lane packs
