@@ -19,9 +19,14 @@ the vector ALU, not HBM: at 5 iterations the method needs about 40
 fp32 operations per element (quant_ops_per_elem below) against a 2-byte input
 element, far above the HBM balance point.  `achieved` is those algorithmic
 operations per second over the kernel's HIP-event time, `peak` the issue rate
-of the fp32 VALUs (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one operation per
-lane per cycle; packed two-wide fp32 instructions are not used), and the
-stage table keeps every kernel's HBM fraction.  `traffic` is the quantiser's
+of fp32 multiply-adds: 256 CUs x 4 SIMDs x 2.4 GHz x 32 lanes, because each
+SIMD can issue two wave64 fp32 FMA/MUL/ADD instructions from different waves
+in one four-cycle slot (157.3 TFLOP/s counting a multiply-add as two; packed
+two-wide fp32 instructions are not used).  Other VALU classes (DPP forms,
+conversions, shifts, min/max, fp16 packed) issue one per slot.  The ALU
+reference kernel (libkvarn_streamref.so) measures the multiply-add rate the
+device sustains at 4 and at 8 waves per SIMD, and the stage table keeps every
+kernel's HBM fraction.  `traffic` is the quantiser's
 measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
 plain device-to-device copy of known size), recorded for the kernel source
 whose SHA-256 prefix is stored beside it; it reads null once the source
@@ -42,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
-VALU_PEAK = 256 * 4 * 16 * 2.4e9   # fp32 VALU lane operations/s (CUs x SIMDs x lanes x clock)
+VALU_PEAK = 256 * 4 * 32 * 2.4e9   # fp32 multiply-add lane operations/s (CUs x SIMDs x dual-issued lanes x clock)
 LAYERS, KV_HEADS, TOKENS, HEAD_DIM, Q_HEADS = 64, 8, 16384, 128, 32
 K_BITS, V_BITS, N_ITERS = 4, 2, 5
 
@@ -66,7 +71,7 @@ def quant_ops_per_elem(D, n_iters):
 # FETCH_SIZE / WRITE_SIZE (scaled by the copy calibration), and the SHA-256
 # prefix of the kernel sources (kernel file + shared device header) they were
 # taken for.
-QUANT_TRAFFIC = {"source_sha256": "a3eff37653832368", "fetch_bytes": 4295729131, "write_bytes": 905969664}
+QUANT_TRAFFIC = {"source_sha256": "957b28c8b5165855", "fetch_bytes": 4295724011, "write_bytes": 906006426}
 QUANT_SOURCE = [os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", f)
                 for f in ("kvarn_quantize.hip", "kvarn_device.hpp")]
 
@@ -280,6 +285,93 @@ def stream_reference(dev, units, reps=5):
     return out
 
 
+def _alu_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_bit_token_amd", "libkvarn_streamref.so"))
+    lib.kvarn_valu_reference.restype = ctypes.c_int
+    lib.kvarn_valu_reference.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p]
+    lib.kvarn_valu_class_reference.restype = ctypes.c_int
+    lib.kvarn_valu_class_reference.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_void_p]
+    lib.kvarn_valu_class_count.restype = ctypes.c_int
+    lib.kvarn_valu_class_name.restype = ctypes.c_char_p
+    lib.kvarn_valu_class_name.argtypes = [ctypes.c_int32]
+    return lib
+
+
+def _best_ms(launch, reps):
+    import torch
+    best = None
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st = launch()
+        e1.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError("ALU reference launch failed: %d" % st)
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return best
+
+
+def alu_reference(dev, iters=4096, reps=3):
+    """Plain fp32 multiply-add chains (libkvarn_streamref.so): the rate the
+    device sustains for the cheapest VALU instructions at 4 waves per SIMD
+    (the quantiser's occupancy) and at 8, in lane operations per second, and
+    the engine clock it ran at (shader-clock over 100 MHz wall-clock ticks)."""
+    import ctypes
+    import torch
+
+    lib = _alu_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    out = {}
+    for waves in (4, 8):
+        blocks = cus * waves          # 256-thread workgroups: one wave per SIMD each
+        buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        ticks = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device=dev)
+        best = _best_ms(lambda: lib.kvarn_valu_reference(buf.data_ptr(), ticks.data_ptr(), blocks,
+                                                         iters, stream), reps)
+        ops = blocks * 256 * iters * 16
+        out["fma_%d_waves_per_simd_Tops" % waves] = round(ops / (best / 1e3) / 1e12, 2)
+        t = ticks.view(-1, 2).double()
+        out["clock_MHz_%d_waves" % waves] = round(float((t[:, 0] / t[:, 1]).mean()) * 100.0, 0)
+        del buf, ticks
+    return out
+
+
+def alu_classes(dev, iters=2048, reps=2):
+    """Issue rate of single VALU instruction classes (16 per loop trip, eight
+    independent registers) at 4 and 8 waves per SIMD: lane operations per
+    second and cycles per wave instruction per SIMD at the measured clock."""
+    import ctypes
+    import torch
+
+    lib = _alu_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    clk = alu_reference(dev)
+    out = {"clock": clk}
+    for cls in range(lib.kvarn_valu_class_count()):
+        name = lib.kvarn_valu_class_name(cls).decode()
+        row = {}
+        for waves in (4, 8):
+            blocks = cus * waves
+            buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            best = _best_ms(lambda: lib.kvarn_valu_class_reference(cls, buf.data_ptr(), blocks,
+                                                                   iters, stream), reps)
+            instr = blocks * 4 * iters * 16             # wave instructions
+            mhz = clk["clock_MHz_%d_waves" % waves]
+            row["%d_waves_Tops" % waves] = round(instr * 64 / (best / 1e3) / 1e12, 2)
+            row["%d_waves_cycles_per_instr" % waves] = round(
+                best / 1e3 * mhz * 1e6 / (instr / (cus * 4)), 2)
+            del buf
+        out[name] = row
+    return out
+
+
 def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
     """Decode attention over the uncompressed fp16 cache of the same workload
     (the baseline of the pages' throughput comparison), timed with HIP events
@@ -423,9 +515,15 @@ def main():
                          "head_dim sweep, attention 64x8x32768)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--alu-classes", action="store_true",
+                    help="run only the per-class VALU issue-rate kernels, print their JSON and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.alu_classes:
+        import torch
+        print(json.dumps(alu_classes(torch.device("cuda:0"))), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the KVarN path on one GPU only; "
@@ -533,6 +631,10 @@ def main():
     if not args.no_stream_ref:
         ref = stream_reference(dev, n_tiles)
         result["stream_reference"] = ref
+        alu = alu_reference(dev)
+        result["roofline"]["alu_reference"] = alu
+        result["roofline"]["frac_of_alu_reference"] = round(
+            achieved / 1e12 / alu["fma_4_waves_per_simd_Tops"], 4)
         for stage, mix in (("quantize", "quantize_mix"), ("dequantize", "dequantize_mix"),
                            ("decode_attention", "packed_read")):
             stages[stage]["achievable_frac"] = round(stages[stage]["hbm_GBps"] / ref[mix]["GBps"], 4)
