@@ -239,7 +239,8 @@ def stream_reference(dev, units, reps=5):
     (libkvarn_streamref.so, built with the library): the rate this device
     delivers for that read/write mix, the reference for each stage's HBM
     fraction beside the nominal 8 TB/s.  Best of a loop kernel and an
-    unrolled one, each at three persistent grid sizes."""
+    unrolled one (with plain and with nontemporal stores), each at three
+    persistent grid sizes."""
     import ctypes
     import torch
 
@@ -260,7 +261,8 @@ def stream_reference(dev, units, reps=5):
     out = {}
     for name, (rq, wq) in mixes.items():
         best = None
-        for per_cu, unrolled in ((4, 0), (8, 0), (16, 0), (4, 1), (8, 1), (16, 1)):
+        for per_cu, unrolled in ((4, 0), (8, 0), (16, 0), (4, 1), (8, 1), (16, 1),
+                                 (4, 2), (8, 2), (16, 2)):
             def run():
                 st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, unrolled,
                         sink.data_ptr(), stream)

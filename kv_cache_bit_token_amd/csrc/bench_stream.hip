@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void stream_mix_kernel(const uint4* __restrict
 
 // The same with the word counts fixed at compile time (loops fully unrolled:
 // a thread's loads all in flight before its stores), for the tile-pair mixes
-// at head_dim 128.
-template <int RQ, int WQ>
+// at head_dim 128.  NT: stores carry the nontemporal hint.
+template <int RQ, int WQ, bool NT>
 __global__ __launch_bounds__(256) void stream_mix_fixed(const uint4* __restrict__ src,
                                                         uint4* __restrict__ dst, int64_t units,
                                                         uint32_t* sink) {
@@ -57,7 +57,15 @@ __global__ __launch_bounds__(256) void stream_mix_fixed(const uint4* __restrict_
 #pragma unroll
             for (int k = 0; k < WL; ++k) {
                 const int i = threadIdx.x + 256 * k;
-                if (i < WQ) d[i] = make_uint4(acc.x ^ (uint32_t)i, acc.y, acc.z, acc.w);
+                if (i < WQ) {
+                    if constexpr (NT) {
+                        using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+                        const u32x4 w = {acc.x ^ (uint32_t)i, acc.y, acc.z, acc.w};
+                        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(d + i));
+                    } else {
+                        d[i] = make_uint4(acc.x ^ (uint32_t)i, acc.y, acc.z, acc.w);
+                    }
+                }
             }
         }
     }
@@ -185,8 +193,9 @@ extern "C" int kvarn_valu_class_reference(int32_t cls, void* out, int32_t blocks
 }
 
 // Streams `units` units through a persistent grid of `blocks` workgroups of
-// 256 threads; with `unrolled` set, the tile-pair mixes at head_dim 128 use
-// the compile-time kernels (others fall back to the loop kernel).  src holds units * rq words, dst units * wq words, sink 256
+// 256 threads; with `unrolled` 1 (2: nontemporal stores), the tile-pair
+// mixes at head_dim 128 use the compile-time kernels (others fall back to the
+// loop kernel).  src holds units * rq words, dst units * wq words, sink 256
 // words; device pointers, 16-byte aligned.  Returns the hipError_t of the
 // launch (0 on success).
 extern "C" int kvarn_stream_reference(const void* src, void* dst, int64_t units, int32_t rq,
@@ -198,22 +207,22 @@ extern "C" int kvarn_stream_reference(const void* src, void* dst, int64_t units,
     const uint4* s4 = static_cast<const uint4*>(src);
     uint4* d4 = static_cast<uint4*>(dst);
     uint32_t* k4 = static_cast<uint32_t*>(sink);
-    if (unrolled && rq == 4096 && wq == 864) {
-        hipLaunchKernelGGL((stream_mix_fixed<4096, 864>), dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units, k4);
-        return (int)hipGetLastError();
+    const bool nt = unrolled == 2;
+#define KVARN_FIXED(RQ_, WQ_)                                                                   \
+    if (unrolled && rq == RQ_ && wq == WQ_) {                                                  \
+        if (nt)                                                                                 \
+            hipLaunchKernelGGL((stream_mix_fixed<RQ_, WQ_, true>), dim3((unsigned)blocks),      \
+                               dim3(256), 0, st, s4, d4, units, k4);                            \
+        else                                                                                    \
+            hipLaunchKernelGGL((stream_mix_fixed<RQ_, WQ_, false>), dim3((unsigned)blocks),     \
+                               dim3(256), 0, st, s4, d4, units, k4);                            \
+        return (int)hipGetLastError();                                                          \
     }
-    if (unrolled && rq == 864 && wq == 4096) {
-        hipLaunchKernelGGL((stream_mix_fixed<864, 4096>), dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units, k4);
-        return (int)hipGetLastError();
-    }
-    if (unrolled && rq == 864 && wq == 0) {
-        hipLaunchKernelGGL((stream_mix_fixed<864, 0>), dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units, k4);
-        return (int)hipGetLastError();
-    }
-    if (unrolled && rq == 4096 && wq == 0) {
-        hipLaunchKernelGGL((stream_mix_fixed<4096, 0>), dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units, k4);
-        return (int)hipGetLastError();
-    }
+    KVARN_FIXED(4096, 864)
+    KVARN_FIXED(864, 4096)
+    KVARN_FIXED(864, 0)
+    KVARN_FIXED(4096, 0)
+#undef KVARN_FIXED
     hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
                        static_cast<uint4*>(dst), units, rq, wq, static_cast<uint32_t*>(sink));

@@ -337,14 +337,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             if constexpr (KW >= 4) {
 #pragma unroll
                 for (int w = 0; w < KW; w += 4) {
-                    const uint4 v = buf_load16(r, kvo + 4 * w, so);
+                    const uint4 v = buf_load16<kPolicyNT>(r, kvo + 4 * w, so);
                     kw[mb][w] = v.x; kw[mb][w + 1] = v.y; kw[mb][w + 2] = v.z; kw[mb][w + 3] = v.w;
                 }
             } else if constexpr (KW == 2) {
-                const uint2 v = buf_load8(r, kvo, so);
+                const uint2 v = buf_load8<kPolicyNT>(r, kvo, so);
                 kw[mb][0] = v.x; kw[mb][1] = v.y;
             } else {
-                kw[mb][0] = buf_load4(r, kvo, so);
+                kw[mb][0] = buf_load4<kPolicyNT>(r, kvo, so);
             }
         }
     };
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         for (int nb = 0; nb < NKB; ++nb) {
             const int so = 16 * nb * VROW;
             if constexpr (VW == 4) {
-                const uint4 v = buf_load16(r, vvo, so);
+                const uint4 v = buf_load16<kPolicyNT>(r, vvo, so);
                 vw[nb][0] = v.x; vw[nb][1] = v.y; vw[nb][2] = v.z; vw[nb][3] = v.w;
             } else {
-                const uint2 v = buf_load8(r, vvo, so);
+                const uint2 v = buf_load8<kPolicyNT>(r, vvo, so);
                 vw[nb][0] = v.x; vw[nb][1] = v.y;
             }
         }

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
             const int so = (int)((st * TS + 16 * mb) * rowb);
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
-                kr[mb][c] = buf_load16(krs, kvo + 64 * c, so);
+                kr[mb][c] = buf_load16<kPolicyNT>(krs, kvo + 64 * c, so);
         }
     };
     auto load_v = [&](int64_t st) {
@@ -142,13 +142,13 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
             for (int e = 0; e < 4; ++e) {
                 const int so = (int)((st * TS + 16 * kb2 + e) * rowb);
                 if constexpr (VCPL == 4) {
-                    const uint2 w = buf_load8(vrs, vvo, so);
+                    const uint2 w = buf_load8<kPolicyNT>(vrs, vvo, so);
                     vr[kb2][e][0] = w.x;
                     vr[kb2][e][1] = w.y;
                 } else {
 #pragma unroll
                     for (int u = 0; u < VCPL / 8; ++u) {
-                        const uint4 w = buf_load16(vrs, vvo + 16 * u, so);
+                        const uint4 w = buf_load16<kPolicyNT>(vrs, vvo + 16 * u, so);
                         vr[kb2][e][4 * u + 0] = w.x;
                         vr[kb2][e][4 * u + 1] = w.y;
                         vr[kb2][e][4 * u + 2] = w.z;

@@ -251,7 +251,9 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
             const int g = ln + 64 * s2;
             const int r = g / CPR, ch = g % CPR;
             const int phys = r * CPR + (ch ^ (((r >> 2) ^ (ch >> 4)) & 1));
-            dst[g] = *reinterpret_cast<const uint4*>(xch + 4 * phys);
+            using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(xch + 4 * phys),
+                                        reinterpret_cast<u32x4*>(dst + g));
         }
     } else if (16 * ob < d0) {
         // padded head_dim: the first d0 channels, straight from registers

@@ -19,14 +19,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Cache-policy bits of a buffer access (gfx940-family encoding): NT marks
+// data that is streamed through once, so it is not kept in the caches.
+constexpr int kPolicyNT = 2;
+
+template <int POL = 0>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
 }
+template <int POL = 0>
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL));
 }
+template <int POL = 0>
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL));
 }
 
 }  // namespace kvarn
