@@ -215,35 +215,58 @@ struct AttnLds {
     __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * G + 16; }
 };
 
+// Natural-order Walsh-Hadamard transform of one D-vector held by one
+// wavefront, lane l owning channels CPL l .. CPL l + CPL - 1 (CPL = D / 64),
+// scaled by 1 / sqrt(D).  Stage h pairs channels j and j + h (j & h == 0)
+// into (x_j + x_{j+h}, x_j - x_{j+h}), h = 1, 2, 4, ...: stages below CPL
+// inside the lane, the others across lanes (partner lane l ^ (h / CPL); the
+// upper member of a pair keeps partner - self).
 template <int D>
-__device__ void lds_fwht(float* v, int rows) {
-    const int tid = threadIdx.x;
-    for (int h = 1; h < D; h <<= 1) {
-        for (int k = tid; k < rows * D / 2; k += blockDim.x) {
-            const int r = k / (D / 2), p = k % (D / 2);
-            const int lo = (p / h) * 2 * h + (p % h), hi = lo + h;
-            const float x = v[r * D + lo], y = v[r * D + hi];
-            v[r * D + lo] = x + y;
-            v[r * D + hi] = x - y;
+__device__ __forceinline__ void wave_fwht(float (&v)[D / 64]) {
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 1; h < CPL; h <<= 1)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if ((c & h) == 0) {
+                const float x = v[c], y = v[c + h];
+                v[c] = x + y;
+                v[c + h] = x - y;
+            }
+#pragma unroll
+    for (int h = CPL; h < D; h <<= 1) {
+        const int lx = h / CPL;
+        const bool upper = (lane & lx) != 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float o = __shfl_xor(v[c], lx);
+            v[c] = upper ? o - v[c] : v[c] + o;
         }
-        __syncthreads();
     }
-    const float s = 1.0f / __builtin_sqrtf((float)D);
-    for (int k = tid; k < rows * D; k += blockDim.x) v[k] *= s;
-    __syncthreads();
+    const float sc = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] *= sc;
 }
 
 // Rotated query of one (b, query head): H q / sqrt(D) over the padded width,
-// once per head for every split that reads it.
+// once per head for every split that reads it.  One wavefront per head, four
+// heads per workgroup.
 template <int D>
-__global__ __launch_bounds__(128) void attn_rotate_q_kernel(AttnArgs a) {
-    __shared__ float v[D];
-    const int bh = blockIdx.x;   // b * n_q_heads + h
-    for (int j = threadIdx.x; j < D; j += blockDim.x)
-        v[j] = (j < a.d0) ? h2f_bits(a.q[(size_t)bh * a.d0 + j]) : 0.0f;
-    __syncthreads();
-    lds_fwht<D>(v, 1);
-    for (int j = threadIdx.x; j < D; j += blockDim.x) a.qrot[(size_t)bh * D + j] = v[j];
+__global__ __launch_bounds__(256) void attn_rotate_q_kernel(AttnArgs a) {
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);   // b * n_q_heads + h
+    if (bh >= a.batch * a.n_q_heads) return;
+    float v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int j = CPL * lane + c;
+        v[c] = (j < a.d0) ? h2f_bits(a.q[(size_t)bh * a.d0 + j]) : 0.0f;
+    }
+    wave_fwht<D>(v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) a.qrot[(size_t)bh * D + CPL * lane + c] = v[c];
 }
 
 template <int D, int KB, int VB, int GMAX>
@@ -626,28 +649,45 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-    __shared__ float o[D];
-    const int tid = threadIdx.x;
-    const int bh = blockIdx.x;   // b * n_q_heads + h
+    // one wavefront per (b, query head), four per workgroup
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);   // b * n_q_heads + h
+    if (bh >= a.batch * a.n_q_heads) return;
     const float* p = a.ws + (size_t)bh * a.n_parts * (D + 2);
+    // global max and the normaliser over the parts (lanes stride the parts)
     float M = -INFINITY;
-    for (int s = 0; s < a.n_parts; ++s) M = fmaxf(M, p[s * (D + 2)]);
+    for (int s = lane; s < a.n_parts; s += 64) M = fmaxf(M, p[(size_t)s * (D + 2)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.0f;
+    for (int s = lane; s < a.n_parts; s += 64) {
+        const float ms = p[(size_t)s * (D + 2)];
+        if (ms != -INFINITY) L += p[(size_t)s * (D + 2) + 1] * exp2f((ms - M) * kLog2e);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    // weighted sum of the parts' accumulators, CPL channels per lane
+    float v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = 0.0f;
     for (int s = 0; s < a.n_parts; ++s) {
-        const float ms = p[s * (D + 2)];
-        if (ms != -INFINITY) L += p[s * (D + 2) + 1] * exp2f((ms - M) * kLog2e);
+        const float* ps = p + (size_t)s * (D + 2);
+        const float ms = ps[0];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f((ms - M) * kLog2e);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(ps[2 + CPL * lane + c], w, v[c]);
     }
-    for (int j = tid; j < D; j += blockDim.x) {
-        float v = 0.0f;
-        for (int s = 0; s < a.n_parts; ++s) {
-            const float ms = p[s * (D + 2)];
-            if (ms != -INFINITY) v += p[s * (D + 2) + 2 + j] * exp2f((ms - M) * kLog2e);
-        }
-        o[j] = (L > 0.0f) ? v / L : 0.0f;
+    const float il = (L > 0.0f) ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] *= il;
+    wave_fwht<D>(v);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int j = CPL * lane + c;
+        if (j < a.d0) a.out[(size_t)bh * a.d0 + j] = v[c];
     }
-    __syncthreads();
-    lds_fwht<D>(o, 1);
-    for (int j = tid; j < a.d0; j += blockDim.x) a.out[(size_t)bh * a.d0 + j] = o[j];
 }
 
 // ---- fp16 tail of a paged sequence (at most 128 tokens, not yet a tile) ----
@@ -830,8 +870,8 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
         // the rotated queries follow the split partials in the workspace
         a.qrot = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) +
                                           qrot_offset(a.batch, a.n_q_heads, D, a.n_parts));
-        hipLaunchKernelGGL((attn_rotate_q_kernel<D>), dim3((unsigned)(a.batch * a.n_q_heads)), dim3(128),
-                           0, s, a);
+        hipLaunchKernelGGL((attn_rotate_q_kernel<D>), dim3((unsigned)((a.batch * a.n_q_heads + 3) / 4)),
+                           dim3(256), 0, s, a);
         hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
         const int per_wave = AttnLds<D>::bytes(G);
@@ -851,7 +891,7 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(a.batch * a.n_q_heads)),
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((a.batch * a.n_q_heads + 3) / 4)),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
