@@ -332,8 +332,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     // Loads run one tile ahead, each issued once its registers are free: the
     // next tile's meta right after this tile's meta is in LDS, its K codes
     // after the q.K^T products, its V codes after the p.V products.  Every
-    // load is unconditional (past the last tile the last one is re-read), so
-    // each wait covers a fixed number of younger loads.
+    // load is unconditional, so each wait covers a fixed number of younger
+    // loads: past the last tile the code loads see an empty buffer range
+    // (zeros, no memory traffic) and the meta is re-read.
     constexpr int KC = 2 * L::KMH / 16, VC = 2 * L::VMH / 16;   // 16-byte meta chunks
     constexpr int MCH = (KC + VC + 63) / 64;                      // chunks per lane
     uint32_t kw[TILE / 16][KW];   // K codes: 8 M-blocks of 16 tokens, one run per lane
@@ -353,7 +354,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int kvo = mrow * KROW + mgrp * (KROW / 4);
     const int vvo = mrow * VROW + mgrp * (VROW / 4);
     auto load_k = [&](int ti) {
-        const auto r = make_rsrc(a.kc + tile_index(ti) * KCB, (uint32_t)KCB);
+        // past the split's last tile the range is empty: the loads return zero
+        // without touching memory, and the wait counts stay the same
+        const auto r = make_rsrc(a.kc + tile_index(ti) * KCB, ti < t1 ? (uint32_t)KCB : 0u);
 #pragma unroll
         for (int mb = 0; mb < TILE / 16; ++mb) {
             const int so = 16 * mb * KROW;
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         }
     };
     auto load_v = [&](int ti) {
-        const auto r = make_rsrc(a.vc + tile_index(ti) * VCB, (uint32_t)VCB);
+        const auto r = make_rsrc(a.vc + tile_index(ti) * VCB, ti < t1 ? (uint32_t)VCB : 0u);
 #pragma unroll
         for (int nb = 0; nb < NKB; ++nb) {
             const int so = 16 * nb * VROW;
