@@ -340,12 +340,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     uint32_t kw[TILE / 16][KW];   // K codes: 8 M-blocks of 16 tokens, one run per lane
     uint32_t vw[NKB][VW];         // V codes: D/16 N-blocks of 16 channels
     uint4 mt[MCH];                // meta chunks
+    // paged cache: the split's first 64 block ids are read once, one per
+    // lane, so a tile's id is a lane read instead of a scalar load on the
+    // prefetch path
+    int blk_lane = 0;
+    if (a.table && t0 + lane < t1) blk_lane = a.table[(size_t)b * a.tiles_per_seq + t0 + lane];
     // pool index of tile ti of this (b, g) (past the split's end: its last
     // tile; a paged table entry outside the pool reads block 0)
     auto tile_index = [&](int ti) -> int64_t {
         const int tc = ti < t1 ? ti : t1 - 1;
         if (!a.table) return (int64_t)bg * a.tiles_per_seq + tc;
-        int64_t blk = a.table[(size_t)b * a.tiles_per_seq + tc];
+        int64_t blk = (tc - t0 < 64) ? __builtin_amdgcn_readlane(blk_lane, tc - t0)
+                                     : a.table[(size_t)b * a.tiles_per_seq + tc];
         if (blk < 0 || blk >= a.pool_blocks) blk = 0;
         return blk * a.n_kv_heads + g;
     };
