@@ -20,9 +20,10 @@
 //    scale/zero absorb the sqrt(D), divided out once per group.
 //  * Log-space accumulation l_c += ln(sigma_c(current values)) gives
 //    exp(l_c) = std over tokens of X'[t][c] * exp(-l_r[t]); the kernel keeps
-//    these products directly (C[c] = exp(l_c), R[t] = exp(l_r)) and
-//    recomputes each std from X' and the current cross-axis factors, the
-//    same quantity without an exp/log round trip.
+//    these factors directly, as reciprocals (1/C[c] = exp(-l_c), 1/R[t] =
+//    exp(-l_r), C and R themselves formed once at the end), and recomputes
+//    each std from X' and the current cross-axis factors: the same quantity
+//    without an exp/log round trip.
 //  * Each std comes from the raw moments sum(v) and sum(v^2) of v = X' * f
 //    (f the cross-axis factor) in one pass; the factor's reciprocal is the
 //    hardware reciprocal square root of the variance (about 1 ulp).  Where
