@@ -216,15 +216,21 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
     fwht_crosslane<R>(x, cb);
 
     // ---- fp16 store ----
-    if constexpr (FULL) {
-        // d0 == D: the wave's 256/R tokens are one contiguous 8 KB run of the
-        // output.  Stage it in the wave's LDS region (16-byte chunks, chunk
-        // index flipped in its lowest bit by token-group parity and by the
-        // upper half of a 512-byte row, so the staging writes of a quarter
-        // wave fall on distinct banks) and store it with fully contiguous
-        // 1 KB wave stores.  The store count is fixed, so the wait for the
-        // next tile's loads need not cover these stores.
-        constexpr int CPR = D / 8;   // 16-byte chunks per token row
+    // The wave's 256/R tokens are one contiguous run of the output (d0
+    // channels per row, 8 KB when d0 == D).  Stage it in the wave's LDS
+    // region as 16-byte chunks and store it with fully contiguous 1 KB wave
+    // stores.  With an even chunk count per row the chunk index is flipped in
+    // its lowest bit by token-group parity and by the upper half of a 512-byte
+    // row, so the staging writes of a quarter wave fall on distinct banks at
+    // d0 == D.  Padded widths stage only their first d0 channels.  The store
+    // count is fixed, so the wait for the next tile's loads need not cover
+    // these stores.
+    {
+        const int CPR = FULL ? D / 8 : d0 / 8;   // 16-byte chunks per output row
+        const bool swz = FULL || (CPR & 1) == 0;
+        auto slot = [&](int r, int ch) {
+            return r * CPR + (swz ? (ch ^ (((r >> 2) ^ (ch >> 4)) & 1)) : ch);
+        };
         const int ln = tid & 63;
         wave_sync();
 #pragma unroll
@@ -232,6 +238,8 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
             const int r = 4 * (ln / R) + i;   // row within the wave's run
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                const int ch = 2 * ob + h;
+                if (!FULL && ch >= CPR) continue;
                 uint32_t o[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -239,36 +247,20 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
                     const uint32_t hi = f2h_bits(x[i][8 * h + 2 * k + 1] * rowscale[i]);
                     o[k] = lo | (hi << 16);
                 }
-                const int ch = 2 * ob + h;
-                const int phys = r * CPR + (ch ^ (((r >> 2) ^ (ch >> 4)) & 1));
-                *reinterpret_cast<uint4*>(xch + 4 * phys) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(xch + 4 * slot(r, ch)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
         wave_sync();
-        uint4* dst = reinterpret_cast<uint4*>(out + (size_t)(tid >> 6) * (256 / R) * D);
+        const int run = (256 / R) * CPR;        // chunks in the wave's run
+        uint4* dst = reinterpret_cast<uint4*>(out + (size_t)(tid >> 6) * (256 / R) * d0);
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) {
             const int g = ln + 64 * s2;
+            if (!FULL && g >= run) break;
             const int r = g / CPR, ch = g % CPR;
-            const int phys = r * CPR + (ch ^ (((r >> 2) ^ (ch >> 4)) & 1));
             using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(xch + 4 * phys),
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(xch + 4 * slot(r, ch)),
                                         reinterpret_cast<u32x4*>(dst + g));
-        }
-    } else if (16 * ob < d0) {
-        // padded head_dim: the first d0 channels, straight from registers
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            uint32_t o[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t lo = f2h_bits(x[i][2 * k] * rowscale[i]);
-                const uint32_t hi = f2h_bits(x[i][2 * k + 1] * rowscale[i]);
-                o[k] = lo | (hi << 16);
-            }
-            uint16_t* dst = out + (size_t)(4 * tb + i) * d0 + 16 * ob;
-            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-            if (16 * ob + 16 <= d0) *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
         }
     }
 }
