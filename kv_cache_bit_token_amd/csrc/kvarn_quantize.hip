@@ -49,6 +49,24 @@ __device__ __forceinline__ uint32_t cvt_u8(float u, uint32_t acc) {
     return __builtin_amdgcn_cvt_pk_u8_f32(u, SEL, acc);
 }
 
+// Sum of v and of v^2 over n values v = x[k] * f[k] of one lane: one
+// rounding per written operation (no contraction), so every caller forms
+// the same bits.
+template <int N>
+__device__ __forceinline__ void lane_moments(const float (&x)[N], const float (&f)[N], float& s1,
+                                             float& s2) {
+#pragma clang fp contract(off)
+    float v = x[0] * f[0];
+    s1 = v;
+    s2 = v * v;
+#pragma unroll
+    for (int k = 1; k < N; ++k) {
+        v = x[k] * f[k];
+        s1 = s1 + v;
+        s2 = __builtin_fmaf(v, v, s2);
+    }
+}
+
 template <int D, int BITS, bool IS_K, bool FULL>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, int d0, int n_iters,
                                               uint8_t* __restrict__ codes_out,
@@ -197,35 +215,81 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
 
         // ---- row pass (V does not use the last one) ----
         if (!IS_K && it == n_iters - 1) break;
+        // Per token: the row-group sums of the moments, each all-reduced
+        // across the R lanes, and the centred fallback where the raw moments
+        // are not accurate (4 mean^2 >= var; uniform across the row-group).
+        auto row_pass_per_token = [&]() {
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const float v0 = x[i][0] * b[0];
-            float s1 = v0, s2 = v0 * v0;
+            for (int i = 0; i < TPL; ++i) {
+                float s1, s2;
+                lane_moments<CPL>(x[i], b, s1, s2);
+                s1 = rg_sum<R>(s1);
+                s2 = rg_sum<R>(s2);
+                const float m2 = s1 * (2.0f / D);   // 2 mean
+                const float t = m2 * m2;            // 4 mean^2
+                const float var = __builtin_fmaf(t, -0.25f, s2 * (1.0f / D));
+                float ai = __builtin_amdgcn_rsqf(var);
+                if (!(t < var)) {
+                    const float mean = 0.5f * m2;
+                    float q = 0.0f;
 #pragma unroll
-            for (int c = 1; c < CPL; ++c) {
-                const float v = x[i][c] * b[c];
-                s1 += v;
-                s2 = __builtin_fmaf(v, v, s2);
-            }
-            s1 = rg_sum<R>(s1);
-            s2 = rg_sum<R>(s2);
-            const float m2 = s1 * (2.0f / D);   // 2 mean
-            const float t = m2 * m2;            // 4 mean^2
-            const float var = __builtin_fmaf(t, -0.25f, s2 * (1.0f / D));
-            float ai = __builtin_amdgcn_rsqf(var);
-            if (!(t < var)) {
-                const float mean = 0.5f * m2;
-                // fallback for this token (uniform across its row-group)
-                float q = 0.0f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const float d = __builtin_fmaf(x[i][c], b[c], -mean);
-                    q = __builtin_fmaf(d, d, q);
+                    for (int c = 0; c < CPL; ++c) {
+                        const float d = __builtin_fmaf(x[i][c], b[c], -mean);
+                        q = __builtin_fmaf(d, d, q);
+                    }
+                    const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
+                    ai = is_flat(sd, mean) ? a[i] : 1.0f / sd;
                 }
-                const float sd = __builtin_sqrtf(rg_sum<R>(q) * (1.0f / D));
-                ai = is_flat(sd, mean) ? a[i] : 1.0f / sd;
+                a[i] = ai;
             }
-            a[i] = ai;
+        };
+        if constexpr (R >= 16) {
+            // D = 256: the reduce-scatter below would cost this width its
+            // occupancy (more VGPRs than 4 waves per SIMD allow)
+            row_pass_per_token();
+        } else {
+            float s1[TPL], s2[TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) lane_moments<CPL>(x[i], b, s1[i], s2[i]);
+            // Reduce-scatter over the xor-1 and xor-2 steps of the row-group
+            // sum, then an all-reduce of the one token left over the xor-7
+            // step (R = 8).  With lane bits c0 c1 c2 of cb, the selectors are
+            // b0 = c0 ^ c2 (tokens 0, 1 stay where b0 = 0, tokens 2, 3 where
+            // b0 = 1) and b1 = c1 ^ c2, so each lane ends with token
+            // u = 2 b0 + b1.  Each selector flips across its own step and
+            // stays fixed across xor 7, so that step pairs lanes holding the
+            // same token.  Every sum pairs the same lanes in the same order as
+            // the per-token all-reduce: the results are the same bits, with 8
+            // cross-lane adds instead of 24 and one reciprocal square root per
+            // lane instead of four.
+            const int c2 = (cb >> 2) & 1;
+            const bool b0 = (cb & 1) ^ c2, b1 = ((cb >> 1) & 1) ^ c2;
+            float r1[2], r2[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                r1[j] = (b0 ? s1[j + 2] : s1[j]) + dpp<DPP_XOR1>(b0 ? s1[j] : s1[j + 2]);
+                r2[j] = (b0 ? s2[j + 2] : s2[j]) + dpp<DPP_XOR1>(b0 ? s2[j] : s2[j + 2]);
+            }
+            float u1 = (b1 ? r1[1] : r1[0]) + dpp<DPP_XOR2>(b1 ? r1[0] : r1[1]);
+            float u2 = (b1 ? r2[1] : r2[0]) + dpp<DPP_XOR2>(b1 ? r2[0] : r2[1]);
+            if constexpr (R >= 8) { u1 += dpp<DPP_HMIR>(u1); u2 += dpp<DPP_HMIR>(u2); }
+            const float m2 = u1 * (2.0f / D);   // 2 mean
+            const float t = m2 * m2;            // 4 mean^2
+            const float var = __builtin_fmaf(t, -0.25f, u2 * (1.0f / D));
+            if (__builtin_amdgcn_ballot_w64(!(t < var)) == 0) {
+                // every token of the wave is accurate: gather the 4 factors
+                const float au = __builtin_amdgcn_rsqf(var);
+                const float g = dpp<DPP_XOR2>(au);                 // token u ^ 1
+                const float A0 = b1 ? g : au, A1 = b1 ? au : g;   // tokens 2 b0, 2 b0 + 1
+                const float h0 = dpp<DPP_XOR1>(A0), h1 = dpp<DPP_XOR1>(A1);
+                a[0] = b0 ? h0 : A0;
+                a[1] = b0 ? h1 : A1;
+                a[2] = b0 ? A0 : h0;
+                a[3] = b0 ? A1 : h1;
+            } else {
+                // some token of the wave needs the centred fallback
+                row_pass_per_token();
+            }
         }
     }
 
