@@ -100,26 +100,23 @@ template <> struct Codes<2> {
     static constexpr float MID = 2.0f;
 };
 
-// (x & mask) | bits in one VALU operation (the compiler otherwise emits an
-// AND and an OR with literal operands); one scalar and one vector constant
-// respect the single scalar read of a VOP3 operation.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
-    return r;
-}
-
 // The magic halves of the SPLIT bit positions, both halves of a dword, held
-// in vector registers for the whole kernel (made opaque to the compiler so it
-// does not rematerialise them at every use).
+// in vector registers for the whole kernel, and the code masks of both
+// halves, held in scalar registers.  Both are made opaque to the compiler so
+// it does not rematerialise them at every use; with the mask in a scalar
+// register, (x & mask) | magic is one v_and_or_b32 (a literal mask would
+// need an AND and an OR).
 template <int B>
 struct CodeMagic {
     uint32_t m[Codes<B>::SPLIT];
+    uint32_t mask[Codes<B>::SPLIT];
     __device__ __forceinline__ void init() {
 #pragma unroll
         for (int i = 0; i < Codes<B>::SPLIT; ++i) {
             const uint32_t f = (25u - (uint32_t)(B * i)) << 10;   // exponent field of 2^(10 - s)
             asm volatile("v_mov_b32 %0, %1" : "=v"(m[i]) : "s"(f | (f << 16)));
+            const uint32_t mk = ((1u << B) - 1u) << (B * i);
+            asm volatile("s_mov_b32 %0, %1" : "=s"(mask[i]) : "i"(mk | (mk << 16)));
         }
     }
 };
@@ -131,8 +128,7 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t wh, int k, co
     const int i = k < C::SPLIT ? k : k - C::SPLIT;
     const int s = B * i;                                      // bit of the code in its half
     const uint32_t x = k < C::SPLIT ? w : wh;
-    const uint32_t mask = ((1u << B) - 1u) << s;
-    const uint32_t v = and_or(x, mask | (mask << 16), cm.m[i]);
+    const uint32_t v = (x & cm.mask[i]) | cm.m[i];
     const _Float16 sub = (_Float16)(-((float)(1 << (10 - s)) + C::MID));
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v) + (h2_t){sub, sub});
 }
