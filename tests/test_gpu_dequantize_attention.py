@@ -85,8 +85,18 @@ def test_attention_oracle_packed(B, n_kv, Hq, T, d0):
     print(compare_attention(out, ref))
 
 
+@pytest.mark.parametrize("B,n_kv,Hq,T,d0", [(1, 2, 12, 384, 64), (2, 1, 6, 256, 256),
+                                            (1, 1, 16, 640, 256), (1, 3, 48, 256, 200),
+                                            (2, 2, 10, 128, 72)])
+def test_attention_group_sizes_and_widths(B, n_kv, Hq, T, d0):
+    # groups of 6, 10, 12 and 16 query heads (the wide-group kernel) at the
+    # other padded widths, ragged head_dims included
+    out, ref = _attention_case(B, n_kv, Hq, T, d0, seed=B * 1000 + Hq * 7 + d0)
+    print(compare_attention(out, ref))
+
+
 def test_attention_other_presets():
-    for kb, vb in ((4, 4), (2, 2)):
+    for kb, vb in ((4, 4), (2, 2), (2, 4)):
         out, ref = _attention_case(1, 2, 8, 256, 128, seed=3, kb=kb, vb=vb)
         print(kb, vb, compare_attention(out, ref))
 
