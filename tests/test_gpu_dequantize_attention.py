@@ -37,7 +37,8 @@ def _gpu_dequant(qk, qv, d0, kb, vb):
 
 @pytest.mark.parametrize("d0,kb,vb", [(128, 4, 2), (128, 4, 4), (128, 2, 2), (128, 2, 4),
                                       (64, 4, 2), (96, 4, 2), (256, 4, 2), (40, 4, 2),
-                                      (200, 4, 2)])
+                                      (200, 4, 2), (64, 2, 4), (256, 4, 4), (96, 2, 2),
+                                      (256, 2, 4)])
 def test_dequantize_oracle_packed(d0, kb, vb):
     _, _, qk, qv = _oracle_cache(6, 2, 384, d0, kb, vb)
     ko, vo = _gpu_dequant(qk, qv, d0, kb, vb)

@@ -60,7 +60,7 @@ def _oracle_pool(seed, pool_blocks, n_kv, d0, kb=4, vb=2):
 
 @pytest.mark.parametrize("B,n_kv,Hq,max_blocks,d0", [(6, 2, 8, 4, 128), (3, 1, 1, 2, 96),
                                                      (4, 4, 64, 3, 64), (4, 8, 32, 3, 256),
-                                                     (5, 2, 4, 1, 128)])
+                                                     (5, 2, 4, 1, 128), (3, 1, 16, 2, 256)])
 def test_paged_attention_oracle_packed(B, n_kv, Hq, max_blocks, d0):
     table, nb, tl, pool = paged_layout(60 + B, B, max_blocks)
     qk, qv = _oracle_pool(61 + B, pool, n_kv, d0)

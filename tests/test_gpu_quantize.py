@@ -58,6 +58,12 @@ def test_other_bit_presets(kb, vb):
     check_pair(kt, vt, kb, vb, 5)
 
 
+@pytest.mark.parametrize("d0,kb,vb", [(64, 2, 4), (256, 4, 4), (96, 2, 2), (256, 2, 4)])
+def test_bit_presets_at_other_widths(d0, kb, vb):
+    k, v = synthetic.outlier_kv_host(9, 2, 256, d0)       # 4 tiles: 2 heads x 2
+    check_pair(synthetic.as_tiles(k), synthetic.as_tiles(v), kb, vb, 5)
+
+
 @pytest.mark.parametrize("n_iters", [0, 1, 3, 16])
 def test_iteration_counts(n_iters):
     kt, vt = _cfg1()
