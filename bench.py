@@ -71,7 +71,7 @@ def quant_ops_per_elem(D, n_iters):
 # FETCH_SIZE / WRITE_SIZE (scaled by the copy calibration), and the SHA-256
 # prefix of the kernel sources (kernel file + shared device header) they were
 # taken for.
-QUANT_TRAFFIC = {"source_sha256": "1753d27cf8d58869", "fetch_bytes": 4295694308, "write_bytes": 906009504}
+QUANT_TRAFFIC = {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295697942, "write_bytes": 906057504}
 QUANT_SOURCE = [os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", f)
                 for f in ("kvarn_quantize.hip", "kvarn_device.hpp")]
 

@@ -67,6 +67,16 @@ __device__ __forceinline__ void lane_moments(const float (&x)[N], const float (&
     }
 }
 
+// One 8-byte LDS read kept apart from its neighbours (the empty asm with a
+// memory clobber stops the compiler from pairing reads into one two-address
+// read: paired reads of the reducer pattern conflict in the LDS banks,
+// single ones do not).
+__device__ __forceinline__ float2 lds_read_single(const float2* p) {
+    const float2 v = *p;
+    asm volatile("" ::: "memory");
+    return v;
+}
+
 template <int D, int BITS, bool IS_K, bool FULL>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, int d0, int n_iters,
                                               uint8_t* __restrict__ codes_out,
@@ -93,10 +103,14 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     constexpr int PST = CPL + 1;
     constexpr int DL = 16 / R;
     float2* part = reinterpret_cast<float2*>(lds);   // [2D][PST]
-    float* colv = lds + 4 * PST * D;                 // [D] broadcast of column stats
-    float* colv2 = colv + D;                         // [D]
-    int* flag = reinterpret_cast<int*>(colv2 + D);   // [1] column-pass fallback request
-    float* gsum = colv2 + D + 4;                     // [16] gauge partials
+    // Broadcast image padded to 20 floats per 16-channel block: the eight
+    // blocks a wavefront reads with 16-byte loads then start on distinct
+    // banks (unpadded, blocks 64 floats apart shared them, two-way).
+    constexpr int CVN = D + D / 4;
+    float* colv = lds + 4 * PST * D;                 // [CVN] broadcast of column stats
+    float* colv2 = colv + CVN;                       // [CVN]
+    int* flag = reinterpret_cast<int*>(colv2 + CVN); // [1] column-pass fallback request
+    float* gsum = colv2 + CVN + 4;                   // [16] gauge partials
 
     // ---------------- load (one HBM read) + pad + first butterfly ----------------
     // FULL: d0 == D, no padding channels
@@ -132,6 +146,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
 
     // reducer role: position p = tid >> 1 (lane-position space), half rh
     const int rp = tid >> 1, rh = tid & 1;
+    const int cwp = rp + 4 * (rp >> 4);   // my reducer position in the padded broadcast image
+    const int crb = 20 * cb;              // my channel block in the padded broadcast image
     const float2* rpart = part + PST * (16 * rh + (rp >> 4)) + (rp & 15);
     float2* wpart = part + PST * tid;
     float Cinv = rsqrtD;   // 1 / column factor of position rp, unscaled units (exp(-l_c) / sqrt(D))
@@ -156,10 +172,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         const float Cinv_prev = Cinv;
         float cmean;
         {
-            float s1 = rpart[0].x, s2 = rpart[0].y;
+            const float2 v0 = lds_read_single(rpart);
+            float s1 = v0.x, s2 = v0.y;
 #pragma unroll
             for (int k = 1; k < 16; ++k) {
-                const float2 v = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
+                const float2 v = lds_read_single(rpart + PST * R * (k % DL + (k / DL) * 2 * DL));
                 s1 += v.x;
                 s2 += v.y;
             }
@@ -176,18 +193,18 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             const float ci = __builtin_amdgcn_rsqf(var);
             Cinv = ok ? ci : Cinv;
             if (!ok) *flag = 1;
-            if (rh == 0) colv[rp] = Cinv;
+            if (rh == 0) colv[cwp] = Cinv;
         }
         __syncthreads();
         if (*flag) {
             // fallback: centred two-pass stds for every column of this pass
             // (the means are those of the raw pass)
-            if (rh == 0) colv2[rp] = cmean;
+            if (rh == 0) colv2[cwp] = cmean;
             __syncthreads();   // every thread has read the flag
             if (tid == 0) *flag = 0;
             float m[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) m[c] = colv2[16 * cb + c];
+            for (int c = 0; c < CPL; ++c) m[c] = colv2[crb + c];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 float q = 0.0f;
@@ -206,12 +223,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
                 q += dpp<DPP_XOR1>(q);
                 const float sd = __builtin_sqrtf(q * (1.0f / TILE));
                 Cinv = is_flat(sd, cmean) ? Cinv_prev : 1.0f / sd;
-                if (rh == 0) colv[rp] = Cinv;
+                if (rh == 0) colv[cwp] = Cinv;
             }
             __syncthreads();
         }
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) b[c] = colv[16 * cb + c];
+        for (int c = 0; c < CPL; ++c) b[c] = colv[crb + c];
 
         // ---- row pass (V does not use the last one) ----
         if (!IS_K && it == n_iters - 1) break;
@@ -337,7 +354,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         {
             float2 v[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = rpart[PST * R * (k % DL + (k / DL) * 2 * DL)];
+            for (int k = 0; k < 16; ++k) v[k] = lds_read_single(rpart + PST * R * (k % DL + (k / DL) * 2 * DL));
             float mn = min3f(v[0].x, v[1].x, v[2].x), mx = max3f(v[0].y, v[1].y, v[2].y);
 #pragma unroll
             for (int k = 3; k < 15; k += 2) {
@@ -351,8 +368,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
             const float sk = range * (1.0f / (float)L);
             const float inv = (range > 0.0f) ? (float)L * __builtin_amdgcn_rcpf(range) : 0.0f;
             if (rh == 0) {
-                colv[rp] = inv;
-                colv2[rp] = -zk * inv;
+                colv[cwp] = inv;
+                colv2[cwp] = -zk * inv;
                 meta_out[kpos] = f2h_bits(sk * rsqrtD * invG);        // SK
                 meta_out[D + kpos] = f2h_bits(zk * rsqrtD * invG);    // ZK
             }
@@ -368,7 +385,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
         }
         float inv[CPL], off[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) { inv[c] = colv[16 * cb + c]; off[c] = colv2[16 * cb + c]; }
+        for (int c = 0; c < CPL; ++c) { inv[c] = colv[crb + c]; off[c] = colv2[crb + c]; }
         // token-major stream: token t, channels 16*ob .. +15 are contiguous
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
@@ -509,10 +526,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ xin, 
     }
 }
 
-// LDS floats: partials [2D][17] float2 + colv/colv2 [2][D] + flag/pad 4 +
-// gauge 16; the V code exchange reuses the front.
+// LDS floats: partials [2D][17] float2 + colv/colv2 [2][D + D/4] + flag/pad
+// 4 + gauge 16; the V code exchange reuses the front.
 template <int D>
-constexpr int quant_lds_floats() { return 4 * (CPL + 1) * D + 2 * D + 4 + 16; }
+constexpr int quant_lds_floats() { return 4 * (CPL + 1) * D + 2 * (D + D / 4) + 4 + 16; }
 
 template <int D, int KB, int VB, bool FULL>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
