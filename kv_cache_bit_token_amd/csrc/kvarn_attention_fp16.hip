@@ -30,8 +30,9 @@
 //
 // Loads run one step ahead: the next step's K right after this step's
 // q.K^T, its V right after this step's p.V; every load is unconditional
-// (clamped token and chunk, selected to zero) so each wait covers a fixed
-// number of younger loads.  A combine kernel merges the splits.
+// (rows past the sequence end read zero through a range-checked descriptor)
+// so each wait covers a fixed number of younger loads.  A combine kernel
+// merges the splits.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 #include "kvarn_rsrc.hpp"
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     constexpr int TS = S::TS, NMB = S::NMB, NCH = S::NCH, NKB = S::NKB, VCPL = S::VCPL;
     constexpr int VW = VCPL / 2;                // dwords of V per lane and token
     const int lane = threadIdx.x & 63;
-    // wave-uniform (scalar) so that the buffer loads take scalar offsets
+    // wave-uniform (scalar) so that the step's descriptors stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int G = a.n_q_heads / a.n_kv_heads;
@@ -110,14 +111,15 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
         }
     }
 
-    // Buffer descriptors of this (b, g)'s K and V rows: a load past the last
-    // row returns zero (no access outside the cache), so the loads of a
-    // partial last step need no clamping.  Per lane the offsets are fixed;
-    // the step and block move only the scalar offset.
+    // Buffer descriptors, one per step: base at the step's first row of this
+    // (b, g), range up to the sequence end.  Every row and chunk offset sits
+    // in the per-lane offset, which the hardware checks against the range
+    // (the scalar offset is not checked, so it stays 0): a load past the last
+    // row returns zero without touching memory, and a partial last step needs
+    // no clamping.
     const int rowb = 2 * d0;
-    const uint32_t nrec = (uint32_t)(T * rowb);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (size_t)bg * T * d0, nrec);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + (size_t)bg * T * d0, nrec);
+    const uint16_t* kbase = a.k + (size_t)bg * T * d0;
+    const uint16_t* vbase = a.v + (size_t)bg * T * d0;
     // K: token 16 mb + mrow, chunk c at byte 16 (4 c + mgrp) of the row
     const int kvo = mrow * rowb + 16 * mgrp;
     // V: token 16 kb + 4 mgrp + e, channels VCPL * mrow ..
@@ -126,29 +128,32 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     uint32_t vr[NMB][4][VW];
     auto load_k = [&](int64_t st) {
         st = st < s1 ? st : s1 - 1;
+        const int64_t r0 = st * TS;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + r0 * d0, (uint32_t)((T - r0) * rowb));
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            const int so = (int)((st * TS + 16 * mb) * rowb);
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
-                kr[mb][c] = buf_load16<kPolicyNT>(krs, kvo + 64 * c, so);
+                kr[mb][c] = buf_load16<kPolicyNT>(r, kvo + 16 * mb * rowb + 64 * c, 0);
         }
     };
     auto load_v = [&](int64_t st) {
         st = st < s1 ? st : s1 - 1;
+        const int64_t r0 = st * TS;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(vbase + r0 * d0, (uint32_t)((T - r0) * rowb));
 #pragma unroll
         for (int kb2 = 0; kb2 < NMB; ++kb2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int so = (int)((st * TS + 16 * kb2 + e) * rowb);
+                const int vo = vvo + (16 * kb2 + e) * rowb;
                 if constexpr (VCPL == 4) {
-                    const uint2 w = buf_load8<kPolicyNT>(vrs, vvo, so);
+                    const uint2 w = buf_load8<kPolicyNT>(r, vo, 0);
                     vr[kb2][e][0] = w.x;
                     vr[kb2][e][1] = w.y;
                 } else {
 #pragma unroll
                     for (int u = 0; u < VCPL / 8; ++u) {
-                        const uint4 w = buf_load16<kPolicyNT>(vrs, vvo + 16 * u, so);
+                        const uint4 w = buf_load16<kPolicyNT>(r, vo + 16 * u, 0);
                         vr[kb2][e][4 * u + 0] = w.x;
                         vr[kb2][e][4 * u + 1] = w.y;
                         vr[kb2][e][4 * u + 2] = w.z;

@@ -2,9 +2,12 @@
 //
 // A descriptor covers one wave-uniform byte range (base and size in scalar
 // registers); loads through it take a per-lane byte offset and a scalar
-// offset, and a load whose range lies past the end returns zero without
-// touching memory.  Kernels keep their per-lane offsets fixed and move the
-// scalar part, which keeps 64-bit address arithmetic off the vector ALU.
+// offset.  Only the per-lane offset (plus the instruction's immediate) is
+// checked against the range: a lane whose offset lies at or past the end
+// reads zero without touching memory, while the scalar offset is added
+// unchecked.  So a kernel may move the scalar offset only inside a range it
+// knows is whole (a full tile); where rows can run past the end, the row
+// offset goes into the per-lane part or the descriptor's base moves.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -212,31 +212,27 @@ def test_python_api_refuses_cpu_tensors(name):
     import torch
     import kv_cache_bit_token_amd as kv
     x = torch.zeros(1, 128, 128, dtype=torch.float16)
+    kc = torch.zeros(1, 8192, dtype=torch.uint8)
+    vc = torch.zeros(1, 4096, dtype=torch.uint8)
+    m = torch.zeros(1, 384, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU tensor"):
         if name == "quantize_tiles":
             kv.quantize_tiles(x, x)
         elif name == "dequantize_tiles":
-            c = torch.zeros(1, 8192, dtype=torch.uint8)
-            m = torch.zeros(1, 384, dtype=torch.float16)
-            kv.dequantize_tiles(c, c, m, m, head_dim=128)
+            kv.dequantize_tiles(kc, vc, m, m, head_dim=128)
         elif name == "decode_attention":
-            c = torch.zeros(1, 8192, dtype=torch.uint8)
-            m = torch.zeros(1, 384, dtype=torch.float16)
-            kv.decode_attention(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m,
+            kv.decode_attention(torch.zeros(1, 4, 128, dtype=torch.float16), kc, vc, m, m,
                                 n_kv_heads=1, tiles_per_seq=1)
         elif name == "quantize_tiles_to":
-            c = torch.zeros(2, 8192, dtype=torch.uint8)
-            m = torch.zeros(2, 384, dtype=torch.float16)
-            kv.quantize_tiles_to(x, x, torch.zeros(1, dtype=torch.int64), c, c, m, m)
+            kv.quantize_tiles_to(x, x, torch.zeros(1, dtype=torch.int64), kc.repeat(2, 1),
+                                 vc.repeat(2, 1), m.repeat(2, 1), m.repeat(2, 1))
         elif name == "decode_attention_fp16":
             t = torch.zeros(1, 1, 128, 128, dtype=torch.float16)
             kv.decode_attention_fp16(torch.zeros(1, 4, 128, dtype=torch.float16), t, t)
         else:
-            c = torch.zeros(1, 8192, dtype=torch.uint8)
-            m = torch.zeros(1, 384, dtype=torch.float16)
             i = torch.zeros(1, 1, dtype=torch.int32)
             t = torch.zeros(1, 1, 128, 128, dtype=torch.float16)
-            kv.decode_attention_paged(torch.zeros(1, 4, 128, dtype=torch.float16), c, c, m, m, i,
+            kv.decode_attention_paged(torch.zeros(1, 4, 128, dtype=torch.float16), kc, vc, m, m, i,
                                       i[0], i[0], t, t, n_kv_heads=1)
 
 
@@ -253,3 +249,53 @@ def test_grid_bounds_refused_on_the_host():
     assert ws(ok, 1 << 20, 32, 8, 1 << 10, ctypes.byref(nb)) == 6   # 2^33 tiles
     fws = lib.kvarn_decode_attention_fp16_workspace
     assert fws(128, 1 << 27, 32, 8, 128, ctypes.byref(nb)) == 6
+
+
+def _api_cases():
+    """(call, expected message) pairs: each passes one buffer whose size does
+    not fit the packed layout or the shape the other arguments imply.  CPU
+    tensors suffice: the binding checks sizes before anything touches a GPU."""
+    import torch
+    import kv_cache_bit_token_amd as kv
+    f16, u8, i32 = torch.float16, torch.uint8, torch.int32
+    x = torch.zeros(2, 128, 128, dtype=f16)
+    c = lambda n, w=8192: torch.zeros(n, w, dtype=u8)
+    vc = lambda n, w=4096: torch.zeros(n, w, dtype=u8)
+    m = lambda n, w=384: torch.zeros(n, w, dtype=f16)
+    q = torch.zeros(2, 8, 128, dtype=f16)
+    t = torch.zeros(2, 2, 128, 128, dtype=f16)
+    i = torch.zeros(2, 3, dtype=i32)
+    n = torch.zeros(2, dtype=i32)
+    return [
+        (lambda: kv.quantize_tiles(x, x, out=(c(1), vc(2), m(2), m(2))), "k_codes must have 2 rows"),
+        (lambda: kv.quantize_tiles(x, x, out=(c(2), vc(2, 8192), m(2), m(2))), "v_codes rows"),
+        (lambda: kv.quantize_tiles(x, x, out=(c(2), vc(2), m(2, 320), m(2))), "k_meta rows"),
+        (lambda: kv.quantize_tiles(x, None, out=(c(2), vc(2), m(2), None)), "v_codes must be given"),
+        (lambda: kv.dequantize_tiles(c(2), vc(2), m(2), m(2), head_dim=64), "k_codes rows"),
+        (lambda: kv.dequantize_tiles(c(2), vc(3), m(2), m(2), head_dim=128), "v_codes must have 2"),
+        (lambda: kv.dequantize_tiles(c(2), vc(2), m(2), m(2), head_dim=128, k_bits=2), "k_codes rows"),
+        (lambda: kv.dequantize_tiles(c(2), vc(2), m(2), None, head_dim=128), "v_codes and v_meta"),
+        (lambda: kv.dequantize_tiles(c(2), vc(2), m(2), m(2), head_dim=128,
+                                     out=(x[:, :, :96], x)), "k out must be"),
+        (lambda: kv.decode_attention(q, c(5), vc(6), m(6), m(6), n_kv_heads=2, tiles_per_seq=3),
+         "k_codes must have at least 12 rows"),
+        (lambda: kv.decode_attention(q, c(12), vc(12), m(12), m(12, 300), n_kv_heads=2,
+                                     tiles_per_seq=3), "v_meta rows"),
+        (lambda: kv.decode_attention(q, c(12), vc(12), m(12), m(12), n_kv_heads=2, tiles_per_seq=3,
+                                     out=torch.zeros(2, 8, 64)), "out must be"),
+        (lambda: kv.quantize_tiles_to(x, x, torch.zeros(2, dtype=torch.int64), c(4), vc(3), m(4),
+                                      m(4)), "v_codes must have 4 rows"),
+        (lambda: kv.quantize_tiles_to(x, x, torch.zeros(2, dtype=torch.int64), c(4), vc(4), m(4),
+                                      m(4, 100)), "v_meta rows"),
+        (lambda: kv.decode_attention_paged(q, c(6), vc(6), m(5), m(6), i, n, n, t, t, n_kv_heads=2),
+         "k_meta must have 6 rows"),
+        (lambda: kv.decode_attention_paged(q, c(5), vc(5), m(5), m(5), i, n, n, t, t, n_kv_heads=2),
+         "pool rows"),
+        (lambda: kv.decode_attention_fp16(q, t, t, out=torch.zeros(2, 4, 128)), "out must be"),
+    ]
+
+
+def test_python_api_checks_buffer_sizes_on_the_host():
+    for call, msg in _api_cases():
+        with pytest.raises(ValueError, match=msg):
+            call()

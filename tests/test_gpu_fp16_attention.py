@@ -58,3 +58,27 @@ def test_fp16_attention_scale_argument():
     torch.cuda.synchronize()
     ref = oracle.decode_attention_fp16(q, k, v, sm_scale=0.05)
     print(compare_attention(out.cpu().numpy(), ref))
+
+
+@pytest.mark.parametrize("B,hkv,hq,T,d0", [
+    (2, 2, 8, 1000, 128),    # ragged last step of 8 of 32 tokens
+    (2, 1, 4, 129, 40),      # head_dim 40 -> 64: 1 of 64 tokens
+    (1, 1, 16, 300, 256),    # 12 of 16 tokens
+])
+def test_fp16_attention_ignores_memory_past_the_cache(B, hkv, hq, T, d0):
+    """K and V are the front of larger buffers whose tail is fp16 NaN: rows
+    past the sequence end must never be read (a stray NaN V row would turn
+    the output NaN through 0 x NaN in p.V)."""
+    q, k, v = _case(B * 100 + T + 7, B, hkv, hq, T, d0)
+    n = k.size
+    spare = 256 * d0   # more than a step of rows
+    bufs = []
+    for x in (k, v):
+        buf = torch.full((n + spare,), float("nan"), dtype=torch.float16, device="cuda")
+        buf[:n] = torch.from_numpy(x.reshape(-1)).cuda()
+        bufs.append(buf[:n].view(B, hkv, T, d0))
+    out = kv.decode_attention_fp16(torch.from_numpy(q).cuda(), bufs[0], bufs[1])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    print(compare_attention(o, oracle.decode_attention_fp16(q, k, v)))
