@@ -1,36 +1,38 @@
 """Benchmark of the KVarN hot path on one MI355X.
 
-Workload: the prefill cache of a 64-layer, 8-KV-head, head_dim-128 model at
-16384 tokens (fp16 K and V of [64*8][16384][128], about 4.3 GB), seeded
-synthetic values with per-layer outlier channels and lognormal token
-magnitudes.  One step runs the whole hot path over it:
+Workload (the step): the prefill cache of a 64-layer, 8-KV-head,
+head_dim-128 model at 16384 tokens (fp16 K and V of [64*8][16384][128],
+about 4.3 GB), seeded synthetic values with per-layer outlier channels and
+lognormal token magnitudes.  One step runs the whole hot path over it:
   1. kvarn_quantize_tiles   (K4V2, 128-token tiles, 5 normalisation iterations)
   2. kvarn_dequantize_tiles (back to fp16)
   3. kvarn_decode_attention (one decode query per layer: 32 query heads over
      the 8 KV heads, all 16384 cached tokens, GQA)
-Inputs are resident in HBM before timing starts.  `value` counts the
-fp16-equivalent KV bytes the step moves through the path (the fp16 K/V fed to
-the quantiser, produced by the dequantiser and represented by the cache the
-attention reads) per second.  Per-stage times come from HIP events recorded on
-the stream the kernels run on.
+Inputs are resident in HBM before timing starts.  `value` is the metric as
+named: fp16 K/V bytes quantised plus fp16 K/V bytes dequantised, per second
+of quantise + dequantise kernel time (the attention stage reads the packed
+cache and is reported beside it, not folded into `value`).  Per-stage times
+come from HIP events recorded on the stream the kernels run on.
 
-The roofline object covers the dominant kernel, the quantiser.  Its bound is
-the vector ALU, not HBM: at 5 iterations the method needs about 40
-fp32 operations per element (quant_ops_per_elem below) against a 2-byte input
+`roofline` covers the dominant kernel, the quantiser.  Its bound is the
+vector ALU, not HBM: at 5 iterations the method needs about 40 fp32
+operations per element (quant_ops_per_elem below) against a 2-byte input
 element, far above the HBM balance point.  `achieved` is those algorithmic
-operations per second over the kernel's HIP-event time, `peak` the issue rate
-of fp32 multiply-adds: 256 CUs x 4 SIMDs x 2.4 GHz x 32 lanes, because each
-SIMD can issue two wave64 fp32 FMA/MUL/ADD instructions from different waves
-in one four-cycle slot (157.3 TFLOP/s counting a multiply-add as two; packed
-two-wide fp32 instructions are not used).  Other VALU classes (DPP forms,
-conversions, shifts, min/max, fp16 packed) issue one per slot.  The ALU
-reference kernel (libkvarn_streamref.so) measures the multiply-add rate the
-device sustains at 4 and at 8 waves per SIMD, and the stage table keeps every
-kernel's HBM fraction.  `traffic` is the quantiser's
-measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
-plain device-to-device copy of known size), recorded for the kernel source
-whose SHA-256 prefix is stored beside it; it reads null once the source
-differs.
+operations per second over the kernel's HIP-event time, `peak` the issue
+rate of fp32 multiply-adds: 256 CUs x 4 SIMDs x 2.4 GHz x 32 lanes, because
+each SIMD can issue two wave64 fp32 FMA/MUL/ADD instructions from different
+waves in one four-cycle slot (157.3 TFLOP/s counting a multiply-add as two;
+packed two-wide fp32 instructions are not used).  `rooflines` holds one
+entry per kernel and workload: the HBM fraction of every kernel (algorithmic
+bytes per launch over its time, against 8 TB/s) and the quantisers' ALU
+fraction.  `traffic` is a kernel's measured HBM bytes per launch (rocprofv3
+FETCH_SIZE + WRITE_SIZE, scaled by a plain device-to-device copy of known
+size), recorded for the kernel sources whose SHA-256 prefix is stored beside
+it; it reads null once a source differs or where no counters were taken.
+
+By default the other workloads run too, kernel by kernel (dequantize
+256 x 8 x 8192, the head_dim sweep, attention 64 x 8 x 32768 and its fp16
+baseline), each with its own roofline entries.
 
 Prints one JSON line.  `--gpus` above 1 exits: this build runs on one GPU.
 `--copy-calibration` instead runs a plain 1 GiB device copy (the reference
@@ -67,13 +69,20 @@ def quant_ops_per_elem(D, n_iters):
     return (k + v) / 2
 
 
-# HBM bytes per launch of the quantiser on this workload, from rocprofv3
-# FETCH_SIZE / WRITE_SIZE (scaled by the copy calibration), and the SHA-256
-# prefix of the kernel sources (kernel file + shared device header) they were
-# taken for.
-QUANT_TRAFFIC = {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295697942, "write_bytes": 906057504}
-QUANT_SOURCE = [os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc", f)
-                for f in ("kvarn_quantize.hip", "kvarn_device.hpp")]
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
+# each with the SHA-256 prefix of the kernel's sources it was taken for.
+TRAFFIC = {
+    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295697942,
+                              "write_bytes": 906057504},
+}
+_CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
+KERNEL_SOURCES = {
+    "quantize": ("kvarn_quantize.hip", "kvarn_device.hpp"),
+    "dequantize": ("kvarn_dequantize.hip", "kvarn_device.hpp"),
+    "decode_attention": ("kvarn_attention.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp"),
+    "fp16_decode_attention": ("kvarn_attention_fp16.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp"),
+}
 
 
 def source_sha(paths):
@@ -84,18 +93,53 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def per_tile_bytes(D):
-    kc = 128 * D * K_BITS // 8
-    vc = 128 * D * V_BITS // 8
-    km = 2 * (2 * D + 128)
-    vm = 2 * (256 + D)
-    fp16 = 2 * 128 * D
-    return {"fp16_pair": 2 * fp16, "packed_pair": kc + vc + km + vm}
+def kernel_sha(kernel):
+    return source_sha([os.path.join(_CSRC, f) for f in KERNEL_SOURCES[kernel]])
+
+
+def measured_traffic(kernel, workload):
+    """Counter-measured HBM bytes per launch, or None when not taken for the
+    current sources."""
+    t = TRAFFIC.get((kernel, workload))
+    if t is None or t["source_sha256"] != kernel_sha(kernel):
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def per_tile_bytes(D, k_bits=K_BITS, v_bits=V_BITS):
+    """fp16 and packed bytes of one K+V tile pair, from the library's own
+    layout query (host only)."""
+    from kv_cache_bit_token_amd import api
+    lay = api.get_layout(D, k_bits, v_bits, 0)
+    packed = lay["k_code_bytes"] + lay["v_code_bytes"] + lay["k_meta_bytes"] + lay["v_meta_bytes"]
+    return {"fp16_pair": 2 * 2 * 128 * D, "packed_pair": packed}
+
+
+def hbm_roofline(kernel, workload, ms, algo_bytes, traffic=None):
+    """HBM roofline entry of one kernel on one workload."""
+    gbs = algo_bytes / (ms / 1e3)
+    return {"kernel": kernel, "workload": workload, "bound": "hbm",
+            "achieved": round(gbs / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK, 4), "traffic": traffic, "algorithmic_bytes": algo_bytes,
+            "ms": round(ms, 4)}
+
+
+def alu_roofline(workload, ms, D, n_iters, elems, traffic=None):
+    """Vector-ALU roofline entry of the quantiser on one workload."""
+    ops = quant_ops_per_elem(D, n_iters) * elems
+    a = ops / (ms / 1e3)
+    return {"kernel": "quantize", "workload": workload, "bound": "alu",
+            "achieved": round(a / 1e12, 3), "peak": round(VALU_PEAK / 1e12, 3), "unit": "Top/s",
+            "frac": round(a / VALU_PEAK, 4), "traffic": traffic,
+            "ops_per_elem": quant_ops_per_elem(D, n_iters), "ms": round(ms, 4)}
 
 
 def cpu_baseline(k, v, q, n_seq, chunk=32):
     """The oracle, untuned, on the first n_seq (layer, head) sequences, fed in
-    chunks of `chunk` sequences (only the oracle calls are timed)."""
+    chunks of `chunk` sequences (only the oracle calls are timed).  `value`
+    is in the unit and sense of the bench's `value`: fp16 K+V bytes quantised
+    plus dequantised per second of quantise + dequantise time; the oracle's
+    decode attention over the same sequences is timed apart."""
     import oracle
 
     threads = len(os.sched_getaffinity(0))
@@ -103,7 +147,7 @@ def cpu_baseline(k, v, q, n_seq, chunk=32):
     tiles_per_seq = TOKENS // 128
     kt_all = k.view(-1, 128, HEAD_DIM)
     vt_all = v.view(-1, 128, HEAD_DIM)
-    dt = 0.0
+    dt = dt_att = 0.0
     for s0 in range(0, n_seq, chunk):
         s1 = min(n_seq, s0 + chunk)
         kt = kt_all[s0 * tiles_per_seq:s1 * tiles_per_seq].cpu().numpy()
@@ -126,23 +170,20 @@ def cpu_baseline(k, v, q, n_seq, chunk=32):
             oracle.decode_attention(qh, qk["codes"][sl], qv["codes"][sl], qk["meta"][sl], qv["meta"][sl],
                                     n_kv_heads=g[1], tiles_per_seq=tiles_per_seq,
                                     k_bits=K_BITS, v_bits=V_BITS)
-            dt += time.perf_counter() - t0
+            dt_att += time.perf_counter() - t0
         del qk, qv, kt, vt
     n_tiles = n_seq * tiles_per_seq
-    fp16_bytes = 3 * n_tiles * per_tile_bytes(HEAD_DIM)["fp16_pair"]
-    # one thread, on the first 512 tokens of the first (layer, head): the same
-    # three stages over its 4 tile pairs
+    fp16_bytes = 2 * n_tiles * per_tile_bytes(HEAD_DIM)["fp16_pair"]
+    # one thread, on the first 512 tokens of the first (layer, head): quantise
+    # and dequantise its 4 tile pairs
     oracle.set_threads(1)
     kt = kt_all[:4].cpu().numpy()
     vt = vt_all[:4].cpu().numpy()
-    qh = q[0:1, 0:Q_HEADS // KV_HEADS].cpu().numpy()
     t0 = time.perf_counter()
     qk = oracle.quantize_tiles(kt, K_BITS, N_ITERS, True)
     qv = oracle.quantize_tiles(vt, V_BITS, N_ITERS, False)
     oracle.dequantize_tiles(qk["codes"], qk["meta"], HEAD_DIM, K_BITS, True)
     oracle.dequantize_tiles(qv["codes"], qv["meta"], HEAD_DIM, V_BITS, False)
-    oracle.decode_attention(qh, qk["codes"], qv["codes"], qk["meta"], qv["meta"], n_kv_heads=1,
-                            tiles_per_seq=4, k_bits=K_BITS, v_bits=V_BITS)
     dt1 = time.perf_counter() - t0
     oracle.set_threads(threads)
     model = ""
@@ -156,12 +197,13 @@ def cpu_baseline(k, v, q, n_seq, chunk=32):
         pass
     return {"value": round(fp16_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 3), "cpu_model": model,
-            "single_thread": {"value": round(3 * 4 * per_tile_bytes(HEAD_DIM)["fp16_pair"] / dt1 / 1e9, 4),
+            "decode_attention_seconds": round(dt_att, 3),
+            "single_thread": {"value": round(2 * 4 * per_tile_bytes(HEAD_DIM)["fp16_pair"] / dt1 / 1e9, 4),
                               "unit": "GB/s", "seconds": round(dt1, 4),
                               "sample": "first 512 tokens of the first (layer, head), 4 tile pairs"},
-            "sample": "%d of %d (layer, head) sequences (%d tile pairs): quantize + dequantize "
-                      "+ decode attention of their query heads, fp64 oracle, same inputs and unit "
-                      "as value" % (n_seq, LAYERS * KV_HEADS, n_tiles)}
+            "sample": "%d of %d (layer, head) sequences (%d tile pairs): quantize + dequantize, fp64 "
+                      "oracle, same inputs and unit as value; decode attention of their query heads "
+                      "timed apart" % (n_seq, LAYERS * KV_HEADS, n_tiles)}
 
 
 def copy_calibration():
@@ -405,21 +447,21 @@ def fp16_attention_measure(kv, k, v, q, packed_out, packed_ms, reps=20):
     nbytes = 2 * k.numel() * 2 + LAYERS * Q_HEADS * HEAD_DIM * (2 + 4)
     rel = float((packed_out - out).norm() / out.norm())
     return {"ms": round(ms, 4), "hbm_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
-            "hbm_frac": round(nbytes / (ms / 1e3) / HBM_PEAK, 4),
+            "hbm_frac": round(nbytes / (ms / 1e3) / HBM_PEAK, 4), "bytes": nbytes,
             "packed_speedup": round(ms / packed_ms, 3),
             "packed_rel_l2": round(rel, 6),
             "workload": "same 64 x 8 x 16384 x 128 cache and queries, uncompressed fp16; "
                         "outside the timed step"}
 
 
-def config_sweep(kv, synthetic, dev, reps=10):
+def config_sweep(kv, synthetic, dev, rooflines, reps=10):
     """The other workloads, timed kernel by kernel with HIP events (inputs
     resident; small working sets rotated across copies totalling > 512 MB so
     the 256 MB last-level cache cannot hold them):
       dequantize         256 seq x 8 KV heads x 8192 tokens x 128 (packed by the quantiser)
       head_dim sweep     8 KV heads x 32768 tokens, head_dim 64 / 96 / 256, 3 and 5 iterations
       decode attention   64 seq x 8 KV heads x 32768 tokens, GQA 32/8, and its fp16 baseline
-    """
+    Appends one roofline entry per kernel and workload to `rooflines`."""
     import torch
 
     def timed(fns):
@@ -442,13 +484,16 @@ def config_sweep(kv, synthetic, dev, reps=10):
 
     out = {}
     # dequantize, 256 x 8 x 8192
+    wl = "dequantize_256x8x8192"
     k, v = synthetic.outlier_kv_torch(1, 256 * 8, 8192, 128, dev)
     kt, vt = k.view(-1, 128, 128), v.view(-1, 128, 128)
     packed = kv.quantize_tiles(kt, vt)
     n = kt.shape[0]
     b = per_tile_bytes(128)
     ms = timed([lambda: kv.dequantize_tiles(*packed, head_dim=128, out=(kt, vt))])
-    out["dequantize_256x8x8192"] = rates(ms, n * b["fp16_pair"], n * (b["fp16_pair"] + b["packed_pair"]), n)
+    hbm = n * (b["fp16_pair"] + b["packed_pair"])
+    out[wl] = rates(ms, n * b["fp16_pair"], hbm, n)
+    rooflines.append(hbm_roofline("dequantize", wl, ms, hbm, measured_traffic("dequantize", wl)))
     del k, v, kt, vt, packed
     torch.cuda.empty_cache()
     # head_dim sweep
@@ -471,10 +516,14 @@ def config_sweep(kv, synthetic, dev, reps=10):
             key = "head_dim_%d_iters_%d" % (d0, it)
             out[key] = {"padded": D, "quantize": rates(ms_q, fp16, fp16 + packed_b, n),
                         "dequantize": rates(ms_d, fp16, fp16 + packed_b, n)}
+            rooflines.append(hbm_roofline("quantize", key, ms_q, fp16 + packed_b))
+            rooflines.append(alu_roofline(key, ms_q, D, it, 2 * n * 128 * D))
+            rooflines.append(hbm_roofline("dequantize", key, ms_d, fp16 + packed_b))
             del outs
         del k, v, kt, vt, ins
         torch.cuda.empty_cache()
     # decode attention, 64 x 8 x 32768, and the fp16 baseline
+    wl = "decode_attention_64x8x32768"
     k, v = synthetic.outlier_kv_torch(5, 64 * 8, 32768, 128, dev)
     kt, vt = k.view(-1, 128, 128), v.view(-1, 128, 128)
     kc, vc, km, vm = kv.quantize_tiles(kt, vt)
@@ -486,14 +535,19 @@ def config_sweep(kv, synthetic, dev, reps=10):
     o = torch.empty((64, 32, 128), dtype=torch.float32, device=dev)
     ms = timed([lambda: kv.decode_attention(q, kc, vc, km, vm, n_kv_heads=8, tiles_per_seq=256,
                                             workspace=ws, out=o)])
-    out["decode_attention_64x8x32768"] = rates(ms, n * b["fp16_pair"], n * b["packed_pair"], n)
+    qb = 64 * 32 * 128 * (2 + 4)
+    out[wl] = rates(ms, n * b["fp16_pair"], n * b["packed_pair"] + qb, n)
+    rooflines.append(hbm_roofline("decode_attention", wl, ms, n * b["packed_pair"] + qb,
+                                  measured_traffic("decode_attention", wl)))
     k4, v4 = k.view(64, 8, 32768, 128), v.view(64, 8, 32768, 128)
     wsf = torch.empty(max(kv.decode_attention_fp16_workspace(batch=64, n_q_heads=32, n_kv_heads=8,
                                                              seq_len=32768, head_dim=128), 16),
                       dtype=torch.uint8, device=dev)
     ms_f = timed([lambda: kv.decode_attention_fp16(q, k4, v4, workspace=wsf, out=o)])
-    out["fp16_decode_attention_64x8x32768"] = rates(ms_f, n * b["fp16_pair"], n * b["fp16_pair"], n)
-    out["fp16_decode_attention_64x8x32768"]["packed_speedup"] = round(ms_f / ms, 3)
+    out["fp16_" + wl] = rates(ms_f, n * b["fp16_pair"], n * b["fp16_pair"] + qb, n)
+    out["fp16_" + wl]["packed_speedup"] = round(ms_f / ms, 3)
+    rooflines.append(hbm_roofline("fp16_decode_attention", wl, ms_f, n * b["fp16_pair"] + qb,
+                                  measured_traffic("fp16_decode_attention", wl)))
     del k, v, kt, vt, kc, vc, km, vm, k4, v4
     torch.cuda.empty_cache()
     return out
@@ -512,9 +566,9 @@ def main():
                     help="skip the fp16-cache decode-attention baseline")
     ap.add_argument("--no-stream-ref", action="store_true",
                     help="skip the streaming reference kernels")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time the other workloads kernel by kernel (dequantize 256x8x8192, "
-                         "head_dim sweep, attention 64x8x32768)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (dequantize 256x8x8192, head_dim sweep, "
+                         "attention 64x8x32768), timed kernel by kernel after the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--alu-classes", action="store_true",
@@ -601,17 +655,27 @@ def main():
                         "hbm_frac": round(gbs / HBM_PEAK, 4),
                         "fp16_equiv_GBps": round(fp16_total / (ms / 1e3) / 1e9, 1),
                         "tile_pairs_per_s": round(n_tiles / (ms / 1e3), 0)}
-    # roofline of the quantiser (the dominant kernel): vector-ALU bound
-    q_ms = stages["quantize"]["ms"]
+    for name in ("quantize", "dequantize"):
+        stages[name]["meets_70pct_hbm_target"] = stages[name]["hbm_frac"] >= 0.70
+    qd_ms = stage_ms[0] + stage_ms[1]
+    wl = "prefill"
     elems = n_tiles * 2 * 128 * HEAD_DIM
-    q_ops = quant_ops_per_elem(HEAD_DIM, N_ITERS) * elems
-    achieved = q_ops / (q_ms / 1e3)
-    traffic = None
-    if QUANT_TRAFFIC["source_sha256"] == source_sha(QUANT_SOURCE):
-        traffic = QUANT_TRAFFIC["fetch_bytes"] + QUANT_TRAFFIC["write_bytes"]
+    # the dominant kernel, the quantiser: vector-ALU bound
+    roofline = alu_roofline(wl, stage_ms[0], HEAD_DIM, N_ITERS, elems,
+                            measured_traffic("quantize", wl))
+    roofline["hbm_frac"] = stages["quantize"]["hbm_frac"]
+    roofline["algorithmic_hbm_bytes"] = hbm["quantize"]
+    rooflines = [
+        roofline,
+        hbm_roofline("quantize", wl, stage_ms[0], hbm["quantize"], measured_traffic("quantize", wl)),
+        hbm_roofline("dequantize", wl, stage_ms[1], hbm["dequantize"],
+                     measured_traffic("dequantize", wl)),
+        hbm_roofline("decode_attention", wl, stage_ms[2], hbm["decode_attention"],
+                     measured_traffic("decode_attention", wl)),
+    ]
     result = {
         "metric": "KV GB/s quantized/dequantized (fp16 in) and % of HBM peak, K4V2 g128",
-        "value": round(3 * fp16_total / (ms_step / 1e3) / 1e9, 2),
+        "value": round(2 * fp16_total / (qd_ms / 1e3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
@@ -620,38 +684,39 @@ def main():
         "config": {"workload": "prefill-cache quantize + dequantize + decode attention, "
                                "64 layers x 8 KV heads x 16384 tokens x head_dim 128, K4V2 g128, "
                                "5 iterations, GQA 32/8",
+                   "value_counts": "fp16 K+V bytes quantised + dequantised per second of "
+                                   "quantise + dequantise kernel time (attention reported apart)",
+                   "hbm_frac_quantize_dequantize": round((hbm["quantize"] + hbm["dequantize"])
+                                                         / (qd_ms / 1e3) / HBM_PEAK, 4),
                    "tiles": n_tiles, "kv_fp16_bytes": fp16_total, "packed_bytes": packed_total},
         "stages": stages,
-        "roofline": {"kernel": "quantize", "bound": "alu", "achieved": round(achieved / 1e12, 3),
-                     "peak": round(VALU_PEAK / 1e12, 3), "unit": "Top/s",
-                     "frac": round(achieved / VALU_PEAK, 4), "traffic": traffic,
-                     "ops_per_elem": quant_ops_per_elem(HEAD_DIM, N_ITERS),
-                     "algorithmic_hbm_bytes": hbm["quantize"],
-                     "hbm_frac": stages["quantize"]["hbm_frac"]},
+        "roofline": roofline,
         "wall_s": round(t_wall, 3),
     }
     if not args.no_stream_ref:
         ref = stream_reference(dev, n_tiles)
         result["stream_reference"] = ref
         alu = alu_reference(dev)
-        result["roofline"]["alu_reference"] = alu
-        result["roofline"]["frac_of_alu_reference"] = round(
-            achieved / 1e12 / alu["fma_4_waves_per_simd_Tops"], 4)
+        roofline["alu_reference"] = alu
+        roofline["frac_of_alu_reference"] = round(
+            roofline["achieved"] / alu["fma_4_waves_per_simd_Tops"], 4)
         for stage, mix in (("quantize", "quantize_mix"), ("dequantize", "dequantize_mix"),
                            ("decode_attention", "packed_read")):
             stages[stage]["achievable_frac"] = round(stages[stage]["hbm_GBps"] / ref[mix]["GBps"], 4)
     if not args.no_fp16:
-        result["fp16_decode_attention"] = fp16_attention_measure(
-            kv, k, v, q, out, stages["decode_attention"]["ms"])
+        f = fp16_attention_measure(kv, k, v, q, out, stages["decode_attention"]["ms"])
+        result["fp16_decode_attention"] = f
+        rooflines.append(hbm_roofline("fp16_decode_attention", wl, f["ms"], f["bytes"],
+                                      measured_traffic("fp16_decode_attention", wl)))
         if "stream_reference" in result:
-            f = result["fp16_decode_attention"]
             f["achievable_frac"] = round(f["hbm_GBps"] / result["stream_reference"]["fp16_read"]["GBps"], 4)
     if not args.no_paged:
         result["paged_decode_attention"] = paged_attention_measure(kv, kc, vc, km, vm, q)
-    if args.configs:
+    if not args.no_configs:
         del ko, vo
         torch.cuda.empty_cache()
-        result["other_workloads"] = config_sweep(kv, synthetic, dev)
+        result["other_workloads"] = config_sweep(kv, synthetic, dev, rooflines)
+    result["rooflines"] = rooflines
     if args.cpu_seqs > 0:
         result["cpu_baseline"] = cpu_baseline(k, v, q, args.cpu_seqs)
     print(json.dumps(result), flush=True)

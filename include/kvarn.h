@@ -92,6 +92,13 @@ kvarn_status kvarn_params_from_preset(const char *preset, int32_t head_dim, int3
                                       kvarn_params *params);
 
 /* Quantise n_tiles tiles of K and of V (rotate, normalise, round, pack, fold).
+ * Defined by: hotdry §Hadamard 旋转 (rotation of every token along the
+ * channels), §迭代方差归一化 (n_iters rounds of column-then-row std
+ * normalisation, factors accumulated in log space), §非对称量化与尺度折叠
+ * (K per channel at k_bits, V per token at v_bits, the group-axis factor
+ * folded into the group's scale and zero point); deep page, worked 2-bit
+ * example (zero point = group min, scale = range / (2^b - 1), code =
+ * round((v - min) / scale)).
  *   k_fp16, v_fp16   [n_tiles][128][head_dim] fp16, device, read only
  *   k_codes, v_codes [n_tiles][k|v_code_bytes] device, written
  *   k_meta, v_meta   [n_tiles][k|v_meta_bytes / 2] fp16, device, written
@@ -104,6 +111,9 @@ kvarn_status kvarn_quantize_tiles(const kvarn_params *params, int64_t n_tiles,
 
 /* Inverse of kvarn_quantize_tiles: unpack, apply the folded scales, undo the
  * rotation, keep the first head_dim channels, round to fp16 (nearest even).
+ * Defined by: hotdry §非对称量化与尺度折叠 (the folded scales restore the
+ * range on read) and §Hadamard 旋转 (the orthonormal transform is its own
+ * inverse); digest §方法 module 3 (the cache is dequantised for attention).
  *   k_out, v_out [n_tiles][128][head_dim] fp16, device, written.
  * Pointer sets (codes, meta, out) of K or V may be all NULL to skip. */
 kvarn_status kvarn_dequantize_tiles(const kvarn_params *params, int64_t n_tiles,
@@ -116,7 +126,12 @@ kvarn_status kvarn_decode_attention_workspace(const kvarn_params *params, int32_
                                               int32_t n_q_heads, int32_t n_kv_heads,
                                               int32_t tiles_per_seq, size_t *bytes);
 
-/* One decode step of GQA attention over the packed cache:
+/* One decode step of GQA attention over the packed cache.  Defined by:
+ * digest §方法 module 3 (attention reads the dequantised cache); deep page,
+ * stage card of the rotation (the orthonormal rotation keeps inner
+ * products, so scores can be taken in the rotated domain) and section
+ * "一次 16K context 的推論，記憶體都花到哪去了" (decode reads the whole cache
+ * each step):
  *   out[b][h] = softmax(sm_scale * q[b][h] . K[b][g]^T) V[b][g],  g = h / (n_q_heads / n_kv_heads)
  * with K, V the dequantised cache (computed on the fly in the rotated domain,
  * never materialised).

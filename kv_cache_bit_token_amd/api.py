@@ -60,7 +60,7 @@ def _rows(t, name, rows, width, exact=True):
     """t must be [rows, ...] with `width` elements per row (at least `rows`
     rows when exact is False).  The C ABI sees only pointers, so this is the
     one place where a buffer too small for the layout is caught."""
-    if t is None:
+    if t is None or (rows == 0 and not exact):   # nothing will be read
         return
     if t.dim() < 1 or (t.shape[0] != rows if exact else t.shape[0] < rows):
         raise ValueError("%s must have %s%d rows (got shape %s)"

@@ -115,8 +115,13 @@ class KvarnCache:
 
 
 def run_probe(steps=2048, head_dim=128, n_q_heads=4, seed=0, beta=0.5, k_bits=4, v_bits=2,
-              n_iters=5, device="cuda"):
-    """-> dict of per-step relative errors (numpy) for the four quantised runs."""
+              n_iters=5, device="cuda", trace=None):
+    """-> dict of per-step relative errors (numpy) for the four quantised runs.
+
+    trace: an optional list that receives, per step, the reference
+    trajectory's tokens (q, k, v as numpy float16), the fp16 reference output
+    and the teacher-forced KVarN output (numpy float32), so that another
+    implementation can replay the same teacher-forced stream."""
     dev = torch.device(device)
     src = FeedbackSource(seed, head_dim, n_q_heads, beta=beta)
     ref = Fp16Cache(steps, head_dim, dev)
@@ -142,6 +147,9 @@ def run_probe(steps=2048, head_dim=128, n_q_heads=4, seed=0, beta=0.5, k_bits=4,
             runs[name].append(kf, vf)
             outs[name] = runs[name].attend(qf[None])[0]
             o_prev[name] = outs[name].cpu().numpy()
+        if trace is not None:
+            trace.append({"q": q.cpu().numpy(), "k": k.cpu().numpy(), "v": v.cpu().numpy(),
+                          "ref": o_ref.cpu().numpy(), "kvarn": outs["kvarn_forced"].cpu().numpy()})
         nr = o_ref.norm()
         rel = torch.stack([(outs[n] - o_ref).norm() / nr for n in runs]).cpu().numpy()
         for i, n in enumerate(runs):

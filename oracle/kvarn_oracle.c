@@ -18,9 +18,10 @@
  * Arithmetic is IEEE double throughout.  Values are rounded to binary16 only
  * where the stored format holds binary16 (scales, zero points, row/column
  * factors, and the dequantised output of the fp16 API).  Each quantisation
- * code is decided in binary32, the precision of the GPU kernel that is
- * compared against this file: the double value u is rounded to float and
- * then to the nearest integer (ties to even).
+ * code is the double value u = (v - min)/scale rounded to the nearest
+ * integer (ties to even), as the worked example defines it; an fp32
+ * implementation may land on the other side where u sits within its
+ * rounding error of a half integer, which is what the parity window is for.
  *
  * Readings of points the pages leave open:
  *   - A tile is 128 tokens x D channels; the rotation runs along channels
@@ -261,9 +262,9 @@ void oracle_rtn_group(const double *v, int n, int stride, int bits,
     *s = scale;
     for (int i = 0; i < n; ++i) {
         double ui = (scale > 0.0) ? (v[(size_t)i * stride] - mn) / scale : 0.0;
-        float r = rintf((float)ui);               /* decided in binary32 */
-        if (r < 0.0f) r = 0.0f;
-        if (r > (float)levels) r = (float)levels;
+        double r = rint(ui);                      /* nearest, ties to even */
+        if (r < 0.0) r = 0.0;
+        if (r > (double)levels) r = (double)levels;
         codes[(size_t)i * cstride] = (uint8_t)r;
         if (u)
             u[(size_t)i * cstride] = ui;

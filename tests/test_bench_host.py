@@ -13,21 +13,30 @@ import bench  # noqa: E402
 
 
 def test_tile_pair_bytes_match_the_stored_format():
-    # K4V2 at head_dim 128: K codes 128*128/2, V codes 128*128/4, K meta
-    # (SK, ZK: D each, RK: 128) and V meta (SV, ZV: 128 each, CV: D) in fp16
+    """bench.py takes its byte counts from the library's layout query; they
+    must equal the oracle's own format sizes, and at K4V2, head_dim 128 the
+    13 824 B per tile pair (0.211x of fp16: the pages' 'under a quarter')."""
+    import oracle
+    for D in (64, 128, 256):
+        for kb, vb in ((4, 2), (4, 4), (2, 2), (2, 4)):
+            b = bench.per_tile_bytes(D, kb, vb)
+            want = (oracle.code_bytes(D, kb) + oracle.code_bytes(D, vb)
+                    + 2 * oracle.meta_halves(D, True) + 2 * oracle.meta_halves(D, False))
+            assert b["packed_pair"] == want, (D, kb, vb)
     b = bench.per_tile_bytes(128)
-    assert b["packed_pair"] == 8192 + 4096 + 2 * (2 * 128 + 128) + 2 * (256 + 128) == 13824
-    assert b["fp16_pair"] == 2 * 2 * 128 * 128 == 65536
-    # the 4.74x byte ratio of K4V2 against fp16
-    assert abs(b["fp16_pair"] / b["packed_pair"] - 4.74) < 0.01
+    assert b["packed_pair"] == 13824 and b["fp16_pair"] == 65536
+    assert bench.per_tile_bytes(64)["packed_pair"] == 7296
+    assert bench.per_tile_bytes(256)["packed_pair"] == 26880
 
 
 def test_quantiser_operation_count():
-    # log2(D) butterflies + 3 per pass (2n passes for K, 2n - 1 for V) + 5 to quantise
-    k = 7 + 3 * 10 + 5
-    v = 7 + 3 * 9 + 5
-    assert bench.quant_ops_per_elem(128, 5) == (k + v) / 2 == 40.5
-    assert bench.quant_ops_per_elem(64, 3) == ((6 + 18 + 5) + (6 + 15 + 5)) / 2
+    # worked by hand from the count stated in bench.quant_ops_per_elem:
+    # D 128, 5 it: K 7 + 30 + 5 = 42, V 7 + 27 + 5 = 39 -> 40.5
+    # D 64, 3 it:  K 6 + 18 + 5 = 29, V 6 + 15 + 5 = 26 -> 27.5
+    # D 256, 5 it: K 8 + 30 + 5 = 43, V 8 + 27 + 5 = 40 -> 41.5
+    assert bench.quant_ops_per_elem(128, 5) == 40.5
+    assert bench.quant_ops_per_elem(64, 3) == 27.5
+    assert bench.quant_ops_per_elem(256, 5) == 41.5
 
 
 def test_alu_peak_is_the_dual_issue_fp32_rate():

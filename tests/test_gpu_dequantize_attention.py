@@ -11,7 +11,7 @@ import torch
 import kv_cache_bit_token_amd as kv
 import oracle
 from kv_cache_bit_token_amd import synthetic
-from parity import compare_attention, compare_dequant
+from parity import compare_attention, compare_dequant, packed_cache, record
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +109,43 @@ def test_attention_empty_cache_is_zero():
     out = kv.decode_attention(q, c, c, m, m, n_kv_heads=2, tiles_per_seq=0)
     torch.cuda.synchronize()
     assert not out.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(512, 8, 32, 13, 128), (1024, 4, 32, 9, 64)])
+def test_attention_several_tiles_per_split(B, n_kv, Hq, tps, d0):
+    """Enough (sequence, KV head) pairs that each split runs several tiles
+    (4096 pairs -> 2 splits per pair: 7 + 6 and 5 + 4 tiles), so the online
+    softmax rescales across a split's tiles and the next-tile prefetch runs
+    inside a split.  The cache is assembled from 256 oracle-quantised tiles of
+    the config-1 recipe, drawn at random per position; the host checks that a
+    later tile of a split often holds a head's largest score, so the running
+    maximum really moves inside splits."""
+    rng = np.random.default_rng(B + d0)
+    k, v = synthetic.outlier_kv_host(B + tps, 2, 128 * 128, d0)
+    kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)      # 256 tiles each
+    qk = oracle.quantize_tiles(kt, 4, 5, True)
+    qv = oracle.quantize_tiles(vt, 2, 5, False)
+    idx = rng.integers(0, kt.shape[0], size=B * n_kv * tps)
+    kc, km = qk["codes"][idx], qk["meta"][idx]
+    vc, vm = qv["codes"][idx], qv["meta"][idx]
+    q = synthetic.query_host(B * 3 + d0, B, Hq, d0)
+    out = kv.decode_attention(_cuda(q), _cuda(kc), _cuda(vc), _cuda(km), _cuda(vm),
+                              n_kv_heads=n_kv, tiles_per_seq=tps)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q, kc, vc, km, vm, n_kv_heads=n_kv, tiles_per_seq=tps)
+    record("attention, several tiles per split %s" % ((B, n_kv, Hq, tps, d0),),
+           compare_attention(out.cpu().numpy(), ref,
+                             packed_cache(q, kc, vc, km, vm, n_kv, tps)))
+    # the first split of each of the first 8 sequences' (KV head, query head):
+    # in how many does the largest score sit past the split's first tile?
+    kd, _ = oracle.dequantize_tiles(qk["codes"], qk["meta"], d0, 4, True)    # [256][128][d0]
+    G, first = Hq // n_kv, (tps + 1) // 2
+    later = total = 0
+    for b in range(8):
+        for g in range(n_kv):
+            tiles = idx[(b * n_kv + g) * tps:(b * n_kv + g) * tps + first]
+            keys = kd[tiles].reshape(-1, d0)
+            s = q[b, g * G:(g + 1) * G].astype(np.float64) @ keys.T
+            later += int((s.argmax(axis=1) >= 128).sum())
+            total += G
+    assert later >= 0.5 * total, (later, total)

@@ -202,3 +202,28 @@ def test_paged_attention_ignores_pool_placement():
     o2 = oracle.decode_attention_paged(q, moved["kc"], moved["vc"], moved["km"], moved["vm"],
                                        table2, nb, tl, kt, vt, n_kv_heads=n_kv)
     assert np.array_equal(o1, o2)
+
+
+def test_fp32_scores_alone_exceed_2e3_at_a_near_tie():
+    """The premise of the attention parity rule's conditioning allowance
+    (tests/parity.py): where two tokens whose values differ by about 2000
+    nearly tie for a score of about 300, rounding the two scores to fp32 and
+    nothing else moves the output by more than 2e-3 against the exact (fp64)
+    attention, so no fp32 evaluation can meet a bare 2e-3 there; the
+    allowance covers the move.  Values are exact in fp16."""
+    from parity import attention_allowance
+    d0 = 128
+    q = np.zeros((1, 1, d0), np.float16)
+    q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 2, d0), np.float16)
+    v = np.zeros((1, 1, 2, d0), np.float16)
+    k[0, 0, 0, 0], k[0, 0, 1, 0] = 3394.0, 3392.0       # scores 299.99 and 299.81
+    v[0, 0, 0, 0], v[0, 0, 1, 0] = 1000.0, -1000.0
+    exact = oracle.decode_attention_fp16(q, k, v)[0, 0]
+    s = (q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T) / np.sqrt(d0)
+    s32 = s.astype(np.float32).astype(np.float64)
+    p = np.exp(s32 - s32.max())
+    o32 = (p / p.sum()) @ v[0, 0].astype(np.float64)
+    move = float(np.abs(o32 - exact).max())
+    assert move > 2e-3
+    assert move <= attention_allowance(q[0], k[0, 0], v[0, 0])[0]

@@ -27,7 +27,7 @@ MUTATIONS = {
     "fold_wrong_axis": ("meta[j] = oracle_double_to_half(exp(lc[j]) * s[j]);           /* SK */",
                         "meta[j] = oracle_double_to_half(exp(lr[j % 128]) * s[j]);           /* SK */"),
     "levels_2b": ("int levels = (1 << bits) - 1;", "int levels = (1 << bits);"),
-    "floor_not_rint": ("float r = rintf((float)ui);", "float r = floorf((float)ui);"),
+    "floor_not_rint": ("double r = rint(ui);", "double r = floor(ui);"),
     "pack_layouts_swapped": ("int64_t e = is_key ? (int64_t)t * D + j : (int64_t)j * TILE + t;\n            int64_t bit = e * bits;\n            out",
                              "int64_t e = !is_key ? (int64_t)t * D + j : (int64_t)j * TILE + t;\n            int64_t bit = e * bits;\n            out"),
     "fwht_sign": ("x[j + h] = a - b;", "x[j + h] = b - a;"),
