@@ -33,8 +33,10 @@
  *     V [SV (128) | ZV (128) | CV (D)].  The rotated-domain value is
  *     K: RK_t * (code * SK_j + ZK_j),  V: CV_j * (code * SV_t + ZV_t).
  *   - Every device pointer must be 16-byte aligned.  Buffers are owned and
- *     allocated by the caller; the library allocates nothing, keeps no global
- *     mutable state, never prints and never aborts.
+ *     allocated by the caller; the library allocates nothing, never prints
+ *     and never aborts.  Its only global state is the static scratch of
+ *     kvarn_decode_attention_noalloc (a device array per GPU and its cached
+ *     device address); every other entry point keeps none.
  *   - Every argument is validated on the host before any launch.  Launches
  *     are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream); nothing synchronises.  A launch failure reported by the HIP
@@ -61,7 +63,7 @@ typedef enum {
     KVARN_E_ITERS = 5,     /* n_iters outside 0..16 */
     KVARN_E_SHAPE = 6,     /* negative or too large a count, or n_q_heads % n_kv_heads != 0 */
     KVARN_E_ALIGN = 7,     /* a pointer is not 16-byte aligned */
-    KVARN_E_WORKSPACE = 8, /* attention workspace too small */
+    KVARN_E_WORKSPACE = 8, /* attention workspace (or the static scratch) too small for the shape */
     KVARN_E_HIP = 9        /* the HIP runtime reported an error at launch */
 } kvarn_status;
 
@@ -146,6 +148,31 @@ kvarn_status kvarn_decode_attention(const kvarn_params *params, int32_t batch,
                                     const void *k_meta, const void *v_meta,
                                     float sm_scale, float *out, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* ---- allocation-free variant, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation) ---- */
+
+/* Bytes of the library's static scratch buffer: one file-scope device array
+ * per GPU, held until the process ends. */
+#define KVARN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* kvarn_decode_attention with its split partials and rotated queries in the
+ * library's static scratch instead of a caller workspace; arguments and
+ * results are those of kvarn_decode_attention.  It allocates nothing: the
+ * scratch of the current device is looked up once per device (the stream
+ * must belong to the current device).  A shape whose workspace
+ * (kvarn_decode_attention_workspace) exceeds KVARN_STATIC_SCRATCH_BYTES is
+ * refused with KVARN_E_WORKSPACE before any launch.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or different host threads without ordering) race; calls in one
+ * stream are ordered.  Nothing in the scratch needs to start at zero. */
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_params *params, int32_t batch,
+                                            int32_t n_q_heads, int32_t n_kv_heads,
+                                            int32_t tiles_per_seq, const void *q_fp16,
+                                            const void *k_codes, const void *v_codes,
+                                            const void *k_meta, const void *v_meta,
+                                            float sm_scale, float *out, void *stream);
 
 /* ---- paged cache (deep page, the section on running inside vLLM's
  * PagedAttention: one 128-token page is one tile and its scales travel with

@@ -11,7 +11,7 @@ __all__ = [
     "quantize_tiles", "dequantize_tiles", "decode_attention",
     "decode_attention_workspace", "get_layout", "params_from_preset", "KvarnError",
     "quantize_tiles_to", "decode_attention_paged", "decode_attention_paged_workspace",
-    "decode_attention_fp16", "decode_attention_fp16_workspace",
+    "decode_attention_fp16", "decode_attention_fp16_workspace", "decode_attention_noalloc",
 ]
 
 

@@ -32,6 +32,8 @@ SIGNATURES = {
     "kvarn_decode_attention": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                               _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
                                               _vp]),
+    "kvarn_decode_attention_noalloc": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                                      _vp, _vp, ctypes.c_float, _vp, _vp]),
     "kvarn_quantize_tiles_to": (ctypes.c_int, [_P, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                                _vp]),
     "kvarn_decode_attention_paged_workspace": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,

@@ -247,6 +247,41 @@ def decode_attention(q, k_codes, v_codes, k_meta, v_meta, *, n_kv_heads, tiles_p
     return out
 
 
+def decode_attention_noalloc(q, k_codes, v_codes, k_meta, v_meta, out, *, n_kv_heads,
+                             tiles_per_seq, k_bits=4, v_bits=2, sm_scale=None):
+    """decode_attention with its scratch in the library's static device buffer:
+    allocates nothing (no workspace; `out`, float32 [batch, n_q_heads,
+    head_dim], is required).  Shapes whose workspace exceeds the static
+    buffer (64 MiB) are refused; calls that overlap on one GPU race."""
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, n_q_heads, head_dim]")
+    batch, hq, head_dim = q.shape
+    lay = get_layout(head_dim, k_bits, v_bits, 0)
+    _cache_rows(k_codes, v_codes, k_meta, v_meta, lay,
+                int(batch) * int(n_kv_heads) * int(tiles_per_seq), False)
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    _shape(out, "out", (batch, hq, head_dim))
+    _need_gpu(q, "q", torch.float16)
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need_gpu(t, name, torch.uint8)
+    for t, name in ((k_meta, "k_meta"), (v_meta, "v_meta")):
+        _need_gpu(t, name, torch.float16)
+    _need_gpu(out, "out", torch.float32)
+    _same_device(q, (k_codes, "k_codes"), (v_codes, "v_codes"), (k_meta, "k_meta"),
+                 (v_meta, "v_meta"), (out, "out"))
+    if sm_scale is None:
+        sm_scale = head_dim ** -0.5
+    lib = _lib.load()
+    p = _params(head_dim, k_bits, v_bits, 0)
+    st = lib.kvarn_decode_attention_noalloc(ctypes.byref(p), batch, hq, int(n_kv_heads),
+                                            int(tiles_per_seq), _ptr(q), _ptr(k_codes),
+                                            _ptr(v_codes), _ptr(k_meta), _ptr(v_meta),
+                                            float(sm_scale), _ptr(out), _stream(q.device))
+    _check("kvarn_decode_attention_noalloc", st)
+    return out
+
+
 def quantize_tiles_to(k, v, dst_tile, k_codes, v_codes, k_meta, v_meta, *, k_bits=4, v_bits=2,
                       n_iters=5):
     """Quantise fp16 K and V tiles into chosen slots of a tile pool.

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libkvarn.so")
 STREAM_SRC = "bench_stream.hip"
 STREAM_LIB = os.path.join(HERE, "libkvarn_streamref.so")
 SOURCES = ["kvarn_abi.cpp", "kvarn_quantize.hip", "kvarn_dequantize.hip", "kvarn_attention.hip",
-           "kvarn_attention_fp16.hip"]
+           "kvarn_attention_fp16.hip", "kvarn_scratch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -52,7 +52,7 @@ const char* kvarn_status_str(kvarn_status s) {
         case KVARN_E_ITERS: return "n_iters must be 0..16";
         case KVARN_E_SHAPE: return "invalid count or head grouping";
         case KVARN_E_ALIGN: return "device pointers must be 16-byte aligned";
-        case KVARN_E_WORKSPACE: return "attention workspace too small";
+        case KVARN_E_WORKSPACE: return "attention workspace (or the static scratch) too small for this shape";
         case KVARN_E_HIP: return "HIP runtime error at launch";
     }
     return "unknown status";
@@ -189,28 +189,39 @@ kvarn_status kvarn_decode_attention_workspace(const kvarn_params* params, int32_
     return KVARN_OK;
 }
 
-kvarn_status kvarn_decode_attention(const kvarn_params* params, int32_t batch, int32_t n_q_heads,
-                                    int32_t n_kv_heads, int32_t tiles_per_seq, const void* q_fp16,
-                                    const void* k_codes, const void* v_codes, const void* k_meta,
-                                    const void* v_meta, float sm_scale, float* out,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by kvarn_decode_attention (caller's workspace) and
+// kvarn_decode_attention_noalloc (the library's static scratch: workspace ==
+// nullptr and use_static set).
+kvarn_status decode_attention_impl(const kvarn_params* params, int32_t batch, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t tiles_per_seq, const void* q_fp16,
+                                   const void* k_codes, const void* v_codes, const void* k_meta,
+                                   const void* v_meta, float sm_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, bool use_static, void* stream) {
     int D = 0;
     kvarn_status st = check_params(params, &D);
     if (st != KVARN_OK) return st;
     st = check_attention_shape(batch, n_q_heads, n_kv_heads, tiles_per_seq);
     if (st != KVARN_OK) return st;
     if (!q_fp16 || !out) return KVARN_E_NULL;
-    if (tiles_per_seq > 0 && (!k_codes || !v_codes || !k_meta || !v_meta || !workspace))
+    if (tiles_per_seq > 0 && (!k_codes || !v_codes || !k_meta || !v_meta || (!workspace && !use_static)))
         return KVARN_E_NULL;
     if (misaligned(q_fp16) || misaligned(out) || misaligned(k_codes) || misaligned(v_codes) ||
         misaligned(k_meta) || misaligned(v_meta) || misaligned(workspace))
         return KVARN_E_ALIGN;
     int ns = 0, tps = 0;
     kvarn::attention_plan(batch, n_kv_heads, tiles_per_seq, &ns, &tps);
-    if (tiles_per_seq > 0 &&
-        workspace_bytes < kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns))
-        return KVARN_E_WORKSPACE;
+    const size_t need = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
+    if (use_static) workspace_bytes = kvarn::kStaticScratchBytes;
+    if (tiles_per_seq > 0 && workspace_bytes < need) return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
+    if (use_static && tiles_per_seq > 0) {
+        // the device address of this GPU's copy of the static array
+        if (kvarn::static_scratch(&workspace) != hipSuccess) return KVARN_E_HIP;
+    }
 
     kvarn::AttnArgs a;
     a.q = static_cast<const uint16_t*>(q_fp16);
@@ -232,6 +243,31 @@ kvarn_status kvarn_decode_attention(const kvarn_params* params, int32_t batch, i
     hipError_t e = kvarn::launch_attention(a, D, params->k_bits, params->v_bits,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVARN_OK : KVARN_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_decode_attention(const kvarn_params* params, int32_t batch, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t tiles_per_seq, const void* q_fp16,
+                                    const void* k_codes, const void* v_codes, const void* k_meta,
+                                    const void* v_meta, float sm_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_attention_impl(params, batch, n_q_heads, n_kv_heads, tiles_per_seq, q_fp16,
+                                 k_codes, v_codes, k_meta, v_meta, sm_scale, out, workspace,
+                                 workspace_bytes, false, stream);
+}
+
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_params* params, int32_t batch,
+                                            int32_t n_q_heads, int32_t n_kv_heads,
+                                            int32_t tiles_per_seq, const void* q_fp16,
+                                            const void* k_codes, const void* v_codes,
+                                            const void* k_meta, const void* v_meta,
+                                            float sm_scale, float* out, void* stream) {
+    return decode_attention_impl(params, batch, n_q_heads, n_kv_heads, tiles_per_seq, q_fp16,
+                                 k_codes, v_codes, k_meta, v_meta, sm_scale, out, nullptr, 0, true,
+                                 stream);
 }
 
 kvarn_status kvarn_quantize_tiles_to(const kvarn_params* params, int64_t n_tiles,

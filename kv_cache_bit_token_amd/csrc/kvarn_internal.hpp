@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvarn.h"
+
 namespace kvarn {
 
 struct QuantArgs {
@@ -77,6 +79,11 @@ struct Fp16AttnArgs {
     int d0;
     float sm_scale;
 };
+
+// Static device scratch of the allocation-free attention entry point: one
+// array per GPU, resolved per device on first use (kvarn_scratch.hip).
+constexpr size_t kStaticScratchBytes = KVARN_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** ptr);
 
 hipError_t launch_quantize(const QuantArgs& a, int D, int kb, int vb, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int D, int kb, int vb, hipStream_t s);

@@ -130,6 +130,26 @@ def test_attention_validation_without_launch():
     assert at(ctypes.byref(P(head_dim=7)), 64, 32, 8, 256, A, A, A, A, A, 0.1, A, A, need, None) == 2
 
 
+def test_noalloc_attention_validation_without_launch():
+    """The allocation-free entry point refuses, before touching any GPU, a
+    shape whose workspace exceeds the static scratch, and validates like
+    kvarn_decode_attention otherwise."""
+    lib = _lib.load()
+    na = lib.kvarn_decode_attention_noalloc
+    ok = ctypes.byref(P())
+    assert na(ok, 0, 32, 8, 256, A, A, A, A, A, 0.1, A, None) == 0        # empty batch
+    assert na(ok, 64, 32, 8, 256, None, A, A, A, A, 0.1, A, None) == 1
+    assert na(ok, 64, 32, 8, 256, A, A, A, None, A, 0.1, A, None) == 1
+    assert na(ok, 64, 32, 8, 256, A, A, A, A, MIS, 0.1, A, None) == 7
+    assert na(ok, 64, 30, 8, 256, A, A, A, A, A, 0.1, A, None) == 6
+    # G = 16, head_dim 256, 8192 pairs of one tile: 8192 * 16 * 258 * 4 B of partials
+    big = ctypes.byref(P(head_dim=256))
+    nb = ctypes.c_size_t()
+    assert lib.kvarn_decode_attention_workspace(big, 8192, 16, 1, 1, ctypes.byref(nb)) == 0
+    assert nb.value > (64 << 20)
+    assert na(big, 8192, 16, 1, 1, A, A, A, A, A, 0.1, A, None) == 8
+
+
 def test_quantize_to_validation_without_launch():
     lib = _lib.load()
     q = lib.kvarn_quantize_tiles_to
