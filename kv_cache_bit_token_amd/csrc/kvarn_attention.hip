@@ -16,27 +16,36 @@
 // Centring the codes keeps both terms of each sum small (ZK is the group
 // minimum, so the uncentred terms would be large and of opposite sign).
 //
-// Matrix cores.  Both contractions run on v_mfma_f32_16x16x32_f16 (two
-// 16-deep operands side by side); the layouts below are those of the 16-deep
-// operands:
-//   q.K^T : A = codes (16 tokens x 16 channels), B = q' (16 channels x the
-//           GQA group's query heads, padded to 16), C = scores;
-//   p.V   : A = p' (query heads x 16 tokens), B = codes (16 tokens x 16
-//           channels), C = partial outputs.
-// Codes become exact fp16 values (c - 2^(b-1)) with a magic-number unpack;
-// q' = qh * SK and p' = p * SV are fp32 values split into fp16 hi + lo
-// parts (each scaled by a power of two per tile), so each product is exact
-// and the fp32 accumulation keeps fp32 accuracy.  The contraction axis is
-// permuted so every lane reads one contiguous run of packed codes: the K
-// row chunk of its token (16 bytes at K4, D = 128) and the V row chunk of
-// its channel (8 bytes at V2); the same permutation orders q' and p'.
+// Integer matrix cores.  Both code contractions run on
+// v_mfma_i32_16x16x64_i8 with the codes as they are (bytes 0 .. 2^b - 1) on
+// one side and the other factor, q' = qh SK per head (or p' = p SV), as a
+// fixed-point integer X = rint(q' 2^f), |X| < 2^27 (2^f a power of two per
+// head and tile), split into four 7-bit limbs X = L3 2^21 + L2 2^14 + L1 2^7
+// + L0 on the other.  The 16 rows of that operand are 4 query heads x 4
+// limbs, so one instruction gives every lane the four limb sums of one
+// (head, token) score or (head, channel) output: exact int32 sums, centred
+// by subtracting mk * sum X (exact, in integers), joined as
+// (L3 2^7 + L2 part) 2^14 + (L1 2^7 + L0 part) with one fp32 rounding.
+//   q.K^T : A = q' limbs (4 heads x 4 limbs) x 64 channels, B = K code bytes
+//           (64 channels x 16 tokens), C = limb sums [head, limb][token];
+//   p.V   : A = p' limbs (4 heads x 4 limbs) x 64 tokens, B = V code bytes
+//           (64 tokens x 16 channels), C = limb sums [head, limb][channel].
+// A lane (row / column l % 16, k-group l / 16) holds 16 bytes of a run of
+// 16 contraction indices; the byte order inside a run follows the cheapest
+// unpack of the packed codes (RunOrder), and the other operand follows it.
+//
+// Token order.  Lane l of a score or output tile holds head l / 16; its
+// column c = l % 16 is, for the scores of 16-token block mb, token
+// tau(mb, c) = r0(c) + delta(mb).  The map is chosen so that the 8 tokens
+// a lane scores are exactly the 8 bytes it contributes to the p.V operand
+// (two dwords of one run), so the softmax runs where the scores land and
+// writes whole dwords of the p' image; the only LDS round trips per tile
+// are the meta, the q' image and the p' image.
 //
 // Work split: each wavefront owns one split (a run of tiles) of one
 // (b, KV head) and every query head of that head's GQA group; waves never
-// synchronise with each other.  Per tile, small per-wave LDS images move
-// q', the scores, p' and the p.V results between the matrix-core layouts and
-// dense layouts in which all 64 lanes do the softmax and the updates.  A
-// combine kernel merges the splits' (max, sum, acc) and undoes the rotation.
+// synchronise with each other.  A combine kernel merges the splits' (max,
+// sum, acc) and undoes the rotation.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 #include "kvarn_rsrc.hpp"
@@ -47,6 +56,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTargetWaves = 8192;   // splits in flight: 8 waves per SIMD on 256 CUs
 constexpr float kLog2e = 1.4426950408889634f;
@@ -80,90 +90,45 @@ size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_p
     return qrot_offset(batch, n_q_heads, D, n_parts) + (size_t)batch * n_q_heads * D * sizeof(float);
 }
 
-// ---- b-bit codes -> exact fp16 (code - 2^(b-1)) -----------------------------
-// A packed dword holds N = 32/b codes.  Pair k takes codes k and k + N/2 (bits
-// b*k and b*k + 16) into the two halves of a dword.  A code sitting at bit s
-// of its half (s + b <= 10) is OR-ed as it stands into the mantissa of a
-// magic fp16 whose unit in the last place is 2^-s, so the half reads
-// magic + code exactly; one packed fp16 add then subtracts magic + 2^(b-1).
-// Only the pairs whose bits lie above the mantissa need a shift, one shared
-// per dword: 4-bit pairs 0, 1 sit at s = 0, 4 and pairs 2, 3 at s = 0, 4 of
-// w >> 8; 2-bit pairs 0..4 at s = 0, 2, 4, 6, 8 and pairs 5..7 at s = 0, 2, 4
-// of w >> 10.
-template <int B> struct Codes;
-template <> struct Codes<4> {
-    static constexpr int N = 8, SPLIT = 2, HI_SHIFT = 8;
-    static constexpr float MID = 8.0f;
+// ---- packed codes -> bytes for the int8 matrix cores -----------------------
+// One run of 16 codes (the 16 contraction indices one lane group gives one
+// instruction) becomes 4 dwords of bytes.
+//   4 bits (two packed dwords w0, w1):  dword 2q + h = (w_q >> 4h) & 0x0F0F0F0F
+//   2 bits (one packed dword w):         dword s      = (w >> 2s) & 0x03030303
+// so byte n of dword j holds run position base(j) + stride * n.
+template <int B> struct RunOrder;
+template <> struct RunOrder<4> {
+    static constexpr int kWords = 2;    // packed dwords per run
+    static constexpr int kStride = 2;
+    __host__ __device__ static constexpr int base(int j) { return 8 * (j / 2) + j % 2; }
 };
-template <> struct Codes<2> {
-    static constexpr int N = 16, SPLIT = 5, HI_SHIFT = 10;
-    static constexpr float MID = 2.0f;
+template <> struct RunOrder<2> {
+    static constexpr int kWords = 1;
+    static constexpr int kStride = 4;
+    __host__ __device__ static constexpr int base(int j) { return j; }
 };
 
-// The magic halves of the SPLIT bit positions, both halves of a dword, held
-// in vector registers for the whole kernel, and the code masks of both
-// halves, held in scalar registers.  Both are made opaque to the compiler so
-// it does not rematerialise them at every use; with the mask in a scalar
-// register, (x & mask) | magic is one v_and_or_b32 (a literal mask would
-// need an AND and an OR).
 template <int B>
-struct CodeMagic {
-    uint32_t m[Codes<B>::SPLIT];
-    uint32_t mask[Codes<B>::SPLIT];
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int i = 0; i < Codes<B>::SPLIT; ++i) {
-            const uint32_t f = (25u - (uint32_t)(B * i)) << 10;   // exponent field of 2^(10 - s)
-            asm volatile("v_mov_b32 %0, %1" : "=v"(m[i]) : "s"(f | (f << 16)));
-            const uint32_t mk = ((1u << B) - 1u) << (B * i);
-            asm volatile("s_mov_b32 %0, %1" : "=s"(mask[i]) : "i"(mk | (mk << 16)));
-        }
+__device__ __forceinline__ v4i_t code_bytes(const uint32_t* w) {
+    if constexpr (B == 4) {
+        return (v4i_t){(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
+                       (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
+    } else {
+        return (v4i_t){(int)(w[0] & 0x03030303u), (int)((w[0] >> 2) & 0x03030303u),
+                       (int)((w[0] >> 4) & 0x03030303u), (int)((w[0] >> 6) & 0x03030303u)};
     }
-};
-
-// pair k of dword w (wh = w >> HI_SHIFT), as two fp16 values code - 2^(b-1)
-template <int B>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t wh, int k, const CodeMagic<B>& cm) {
-    using C = Codes<B>;
-    const int i = k < C::SPLIT ? k : k - C::SPLIT;
-    const int s = B * i;                                      // bit of the code in its half
-    const uint32_t x = k < C::SPLIT ? w : wh;
-    const uint32_t v = (x & cm.mask[i]) | cm.m[i];
-    const _Float16 sub = (_Float16)(-((float)(1 << (10 - s)) + C::MID));
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v) + (h2_t){sub, sub});
 }
 
-// Matrix operand kb (4 fp16 values) out of a lane's run of packed dwords.
-// Operand kb uses dword d = kb / (N/4) and pairs 2*k2, 2*k2 + 1 (k2 = kb mod
-// N/4); element e holds code 2*k2 + (e >> 1) + (N/2)*(e & 1) of that dword.
-template <int B, int NW>
-__device__ __forceinline__ h4_t code_operand(const uint32_t (&w)[NW], int kb, const CodeMagic<B>& cm) {
-    constexpr int Q = Codes<B>::N / 4;
-    const int d = kb / Q, k2 = kb % Q;
-    const uint32_t wh = w[d] >> Codes<B>::HI_SHIFT;
-    const uint32_t lo = code_pair<B>(w[d], wh, 2 * k2, cm);
-    const uint32_t hi = code_pair<B>(w[d], wh, 2 * k2 + 1, cm);
-    return __builtin_bit_cast(h4_t, make_uint2(lo, hi));
-}
+// Token of column c in 16-token block mb (tau = r0(c) + delta(mb)): column c
+// = 4 g + j owns dword j of lane group g's two p.V runs (tokens 32 g + 16 m
+// + base(j) + stride n, m = mb / 4, n = mb % 4), so its 8 scores are the 8
+// bytes it writes into the p' image.
+template <int VB>
+__device__ __forceinline__ int tok_r0(int c) { return 32 * (c >> 2) + RunOrder<VB>::base(c & 3); }
+template <int VB>
+__host__ __device__ constexpr int tok_delta(int mb) { return 16 * (mb >> 2) + RunOrder<VB>::kStride * (mb & 3); }
 
-// Two 16-deep operands side by side as one 32-deep operand of
-// v_mfma_f32_16x16x32_f16.  A and B pair their elements by (lane group,
-// element) alike, so concatenating operands 2j and 2j + 1 on both sides sums
-// exactly the products the two 16-deep instructions summed.
-__device__ __forceinline__ h8_t cat8(h4_t x, h4_t y) {
-    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Runs of a dense task that covers operands kbase, kbase + 1 (kbase even) of a
-// lane group: the 8 elements are run0 + 0..3 and run1 + 0..3, stored
-// interleaved [r0_0, r1_0, r0_1, r1_1, r0_2, r1_2, r0_3, r1_3].
-template <int B>
-__device__ __forceinline__ int run0_of(int group_base, int kbase) {
-    constexpr int N = Codes<B>::N, Q = N / 4;
-    return group_base + N * (kbase / Q) + 2 * (kbase % Q);
-}
-
-// reductions over aligned groups of W lanes (W = 8, 16, 32)
+// reductions over aligned groups of W lanes (W = 8, 16, 32, 64)
 template <int W>
 __device__ __forceinline__ float grp_sum(float v) {
     v += dpp<DPP_XOR1>(v);
@@ -171,6 +136,7 @@ __device__ __forceinline__ float grp_sum(float v) {
     v += dpp<DPP_HMIR>(v);
     if constexpr (W >= 16) v += dpp<DPP_ROR8>(v);
     if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
     return v;
 }
 template <int W>
@@ -180,35 +146,81 @@ __device__ __forceinline__ float grp_max(float v) {
     v = fmaxf(v, dpp<DPP_HMIR>(v));
     if constexpr (W >= 16) v = fmaxf(v, dpp<DPP_ROR8>(v));
     if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int W>
+__device__ __forceinline__ int grp_isum(int v) {
+    v += dpp_i<DPP_XOR1>(v);
+    v += dpp_i<DPP_XOR2>(v);
+    v += dpp_i<DPP_HMIR>(v);
+    if constexpr (W >= 16) v += dpp_i<DPP_ROR8>(v);
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
     return v;
 }
 
-// power-of-two scale s with max * s < 2^10 (1 for max == 0)
-__device__ __forceinline__ float pow2_scale(float mx) {
+// power-of-two scale s with max * s in [2^26, 2^27) (1 for max == 0): the
+// fixed-point range of the four 7-bit limbs
+__device__ __forceinline__ float fx_scale(float mx) {
     if (!(mx > 0.0f)) return 1.0f;
     int e;
     (void)frexpf(mx, &e);          // mx = m * 2^e, m in [0.5, 1)
-    return ldexpf(1.0f, 10 - e);
+    return ldexpf(1.0f, 27 - e);
 }
 
-__device__ __forceinline__ void split_hi_lo(float x, _Float16& hi, _Float16& lo) {
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
+// x = rint(v * s), |x| < 2^27, as hi = x >> 14 = L3 2^7 + L2 and lo = x & 0x3FFF = L1 2^7 + L0
+__device__ __forceinline__ void fx_split(float v, float s, int& hi, int& lo) {
+    const int x = (int)__builtin_rintf(v * s);
+    hi = x >> 14;
+    lo = x & 0x3FFF;
 }
 
-// Per-wave LDS layout (bytes), for GQA group size G (padded to GP = 4k).
+// low bytes of a0 .. a3 -> bytes 0 .. 3 of one dword
+__device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
+    const uint32_t x = __builtin_amdgcn_perm((uint32_t)a1, (uint32_t)a0, 0x0c0c0400u);
+    const uint32_t y = __builtin_amdgcn_perm((uint32_t)a3, (uint32_t)a2, 0x04000c0cu);
+    return x | y;
+}
+
+// The four limb dwords (L0, L1, L2, L3; byte n = value n) of four split values.
+__device__ __forceinline__ void limb_dwords(const int (&hi)[4], const int (&lo)[4], uint32_t (&d)[4]) {
+    d[0] = pack4(lo[0] & 127, lo[1] & 127, lo[2] & 127, lo[3] & 127);
+    d[1] = pack4(lo[0] >> 7, lo[1] >> 7, lo[2] >> 7, lo[3] >> 7);
+    d[2] = pack4(hi[0] & 127, hi[1] & 127, hi[2] & 127, hi[3] & 127);
+    d[3] = pack4(hi[0] >> 7, hi[1] >> 7, hi[2] >> 7, hi[3] >> 7);
+}
+
+// Limb sums c[i] = sum L_i * code of one (head, index), centred by the exact
+// integer sums t_hi = mid * sum (x >> 14), t_lo = mid * sum (x & 0x3FFF):
+// sum x (code - mid) = ((c3 2^7 + c2) - t_hi) 2^14 + ((c1 2^7 + c0) - t_lo).
+__device__ __forceinline__ float limb_join(v4i_t c, int t_hi, int t_lo) {
+    const int hi = (c[3] << 7) + c[2] - t_hi;
+    const int lo = (c[1] << 7) + c[0] - t_lo;
+    return __builtin_fmaf((float)hi, 16384.0f, (float)lo);
+}
+
+// Per-wave LDS layout (bytes), for GQA group size G (RB = ceil(G / 4) row
+// blocks of 4 heads): the tile's meta (K then V, adjacent), the q' limb
+// image [rb][kc][lane][16 B] and the p' limb image [rb][m][lane][16 B] (both
+// in the matrix-core operand layout, one 16-byte read per lane), and four
+// per-head scalars of the scores (zero-point term, 1 / scale, two centring
+// sums).
 template <int D>
 struct AttnLds {
     static constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
-    static constexpr int NKB = D / 16;
+    static constexpr int NKC = D / 64;          // 64-channel runs of q.K^T per M-block
+    __host__ __device__ static constexpr int rb(int G) { return (G + 3) / 4; }
     __host__ __device__ static constexpr int kmeta(int) { return 0; }
     __host__ __device__ static constexpr int vmeta(int) { return 2 * KMH; }
-    __host__ __device__ static constexpr int bq(int) { return 2 * KMH + 2 * VMH; }
-    __host__ __device__ static constexpr int sc(int G) { return bq(G) + 64 * G * NKB; }
-    __host__ __device__ static constexpr int pa(int G) { return sc(G) + 512 * G; }
-    __host__ __device__ static constexpr int pvc(int G) { return pa(G) + 512 * G; }
-    __host__ __device__ static constexpr int stats(int G) { return pvc(G) + 4 * D * ((G + 3) & ~3); }
-    __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * G + 16; }
+    __host__ __device__ static constexpr int qa(int) { return 2 * KMH + 2 * VMH; }
+    __host__ __device__ static constexpr int pa(int G) { return qa(G) + rb(G) * NKC * 1024; }
+    __host__ __device__ static constexpr int stats(int G) { return pa(G) + rb(G) * 2 * 1024; }
+    __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * 4 * rb(G); }
 };
 
 // Natural-order Walsh-Hadamard transform of one D-vector held by one
@@ -268,18 +280,18 @@ __global__ __launch_bounds__(256) void attn_rotate_q_kernel(AttnArgs a) {
 template <int D, int KB, int VB, int GMAX>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     using L = AttnLds<D>;
-    constexpr int NKB = D / 16;                 // q.K^T operands per M-block (channels)
-    constexpr int NVB = TILE / 16;              // p.V operands per N-block (tokens)
+    constexpr int NKC = D / 64;                 // 64-channel runs of q.K^T per M-block
+    constexpr int NNB = D / 16;                 // 16-channel N-blocks of p.V
     constexpr int KROW = D * KB / 8;            // packed bytes of one token's K row
     constexpr int VROW = TILE * VB / 8;         // packed bytes of one channel's V row
     constexpr int KW = KROW / 16;               // dwords of a lane group's K chunk
     constexpr int VW = VROW / 16;               // dwords of a lane group's V chunk
+    constexpr int KRW = RunOrder<KB>::kWords, VRW = RunOrder<VB>::kWords;
     constexpr int KCB = TILE * KROW, VCB = D * VROW;
-    constexpr int QT = D / 8;                   // dense tasks per query (channels)
-    constexpr int QTMAX = (GMAX * QT + 63) / 64;
-    constexpr int STMAX = (GMAX * 16 + 63) / 64;
-    constexpr int CPL_E = D / 64;               // epilogue channels per lane
-    constexpr float MK = Codes<KB>::MID, MV = Codes<VB>::MID;
+    constexpr int RBMAX = GMAX / 4;             // row blocks of 4 query heads
+    constexpr int QPH = D / 4;                  // q' tasks per head (4 channels each)
+    constexpr int QR = (GMAX * QPH + 63) / 64;  // q' tasks per lane
+    constexpr int MK = 1 << (KB - 1), MV = 1 << (VB - 1);
 
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63;
@@ -287,7 +299,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int G = a.n_q_heads / a.n_kv_heads;
-    const int GP = (G + 3) & ~3;
+    const int RB = (G + 3) >> 2;
     const int sgroups = (a.n_splits + wpb - 1) / wpb;
     const int bg = blockIdx.x / sgroups;
     const int split = (blockIdx.x % sgroups) * wpb + wave;
@@ -311,19 +323,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     uint8_t* lds = smem + (size_t)wave * L::bytes(G);
     uint16_t* kmeta = reinterpret_cast<uint16_t*>(lds + L::kmeta(G));
     uint16_t* vmeta = reinterpret_cast<uint16_t*>(lds + L::vmeta(G));
-    uint8_t* bqimg = lds + L::bq(G);
-    float* sc = reinterpret_cast<float*>(lds + L::sc(G));
+    uint8_t* qaimg = lds + L::qa(G);
     uint8_t* paimg = lds + L::pa(G);
-    float* pvc = reinterpret_cast<float*>(lds + L::pvc(G));
-    float* st = reinterpret_cast<float*>(lds + L::stats(G));
-    float* st_qz = st;              // [G] zero-point term of the scores
-    float* st_iq = st + G;          // [G] 1 / q' scale
-    float* st_al = st + 2 * G;      // [G] softmax rescale of this tile
-    float* st_pz = st + 3 * G;      // [G] zero-point term of p.V
-    float* st_ip = st + 4 * G;      // [1] 1 / p' scale
+    float* st_qz = reinterpret_cast<float*>(lds + L::stats(G));   // [4 RB] zero-point term
+    float* st_iq = st_qz + 4 * RB;                                   // [4 RB] 1 / q' scale
+    int* st_th = reinterpret_cast<int*>(st_iq + 4 * RB);            // [4 RB] centring, hi part
+    int* st_tl = st_th + 4 * RB;                                     // [4 RB] centring, lo part
 
-    const int mrow = lane & 15;     // MFMA row / column index of this lane
-    const int mgrp = lane >> 4;     // MFMA k-group of this lane
+    const int col = lane & 15;      // matrix-core row / column of this lane
+    const int lgr = lane >> 4;      // matrix-core lane group: head of a score or output tile
 
     // Loads run one tile ahead, each issued once its registers are free: the
     // next tile's meta right after this tile's meta is in LDS, its K codes
@@ -333,8 +341,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     // (zeros, no memory traffic) and the meta is re-read.
     constexpr int KC = 2 * L::KMH / 16, VC = 2 * L::VMH / 16;   // 16-byte meta chunks
     constexpr int MCH = (KC + VC + 63) / 64;                      // chunks per lane
-    uint32_t kw[TILE / 16][KW];   // K codes: 8 M-blocks of 16 tokens, one run per lane
-    uint32_t vw[NKB][VW];         // V codes: D/16 N-blocks of 16 channels
+    uint32_t kw[TILE / 16][KW];   // K codes: 8 blocks of 16 tokens, one chunk per lane
+    uint32_t vw[NNB][VW];         // V codes: D/16 N-blocks of 16 channels
     uint4 mt[MCH];                // meta chunks
     // paged cache: the split's first 64 block ids are read once, one per
     // lane, so a tile's id is a lane read instead of a scalar load on the
@@ -352,16 +360,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         return blk * a.n_kv_heads + g;
     };
     // codes through per-tile buffer descriptors: per-lane offsets fixed, the
-    // block moves the scalar offset
-    const int kvo = mrow * KROW + mgrp * (KROW / 4);
-    const int vvo = mrow * VROW + mgrp * (VROW / 4);
+    // block moves the scalar offset (every read stays inside the whole tile)
+    const int kvo = tok_r0<VB>(col) * KROW + lgr * (KROW / 4);   // token tau(., col), lane group lgr
+    const int vvo = col * VROW + lgr * (VROW / 4);               // channel col, lane group lgr
     auto load_k = [&](int ti) {
         // past the split's last tile the range is empty: the loads return zero
         // without touching memory, and the wait counts stay the same
         const auto r = make_rsrc(a.kc + tile_index(ti) * KCB, ti < t1 ? (uint32_t)KCB : 0u);
 #pragma unroll
         for (int mb = 0; mb < TILE / 16; ++mb) {
-            const int so = 16 * mb * KROW;
+            const int so = tok_delta<VB>(mb) * KROW;
             if constexpr (KW >= 4) {
 #pragma unroll
                 for (int w = 0; w < KW; w += 4) {
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     auto load_v = [&](int ti) {
         const auto r = make_rsrc(a.vc + tile_index(ti) * VCB, ti < t1 ? (uint32_t)VCB : 0u);
 #pragma unroll
-        for (int nb = 0; nb < NKB; ++nb) {
+        for (int nb = 0; nb < NNB; ++nb) {
             const int so = 16 * nb * VROW;
             if constexpr (VW == 4) {
                 const uint4 v = buf_load16<kPolicyNT>(r, vvo, so);
@@ -402,49 +410,44 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             mt[r] = *src;
         }
     };
+    // q' tasks: task t = lane + 64 r covers head n = t / QPH and the 4
+    // channels of dword j of run (lane group gq, chunk kc):
+    //   channel gq D/4 + 16 kc + base(j) + stride n', n' = 0..3
     // The group's rotated queries (H q / sqrt(D), from the rotation kernel)
-    // and then the first tile go out before anything waits.
-    // task t: query n = t / QT; lane group gq = (t % QT) / (NKB / 2); pair pr
-    float qh[QTMAX][8];
+    // at those channels, and then the first tile, go out before anything waits.
+    float qh[QR][4];
 #pragma unroll
-    for (int r = 0; r < QTMAX; ++r) {
+    for (int r = 0; r < QR; ++r) {
         const int t = lane + 64 * r;
-        const int n = t / QT, rem = t % QT;
-        const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
-        const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
-        const float* src = a.qrot + ((size_t)b * a.n_q_heads + g * G + (n < G ? n : G - 1)) * D;
-        const float4 lo = *reinterpret_cast<const float4*>(src + r0);
-        const float4 hi = *reinterpret_cast<const float4*>(src + r1);
+        const int n = t / QPH, rem = t % QPH;
+        const int gq = rem / (D / 16), rem2 = rem % (D / 16);
+        const int kc = rem2 >> 2, j = rem2 & 3;
         const bool live = n < G;
-        qh[r][0] = live ? lo.x : 0.0f; qh[r][1] = live ? lo.y : 0.0f;
-        qh[r][2] = live ? lo.z : 0.0f; qh[r][3] = live ? lo.w : 0.0f;
-        qh[r][4] = live ? hi.x : 0.0f; qh[r][5] = live ? hi.y : 0.0f;
-        qh[r][6] = live ? hi.z : 0.0f; qh[r][7] = live ? hi.w : 0.0f;
+        const float* src = a.qrot + ((size_t)b * a.n_q_heads + g * G + (live ? n : 0)) * D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ch = gq * (D / 4) + 16 * kc + RunOrder<KB>::base(j) + RunOrder<KB>::kStride * e;
+            qh[r][e] = live ? src[ch] : 0.0f;
+        }
     }
     load_meta(t0);
     load_k(t0);
     load_v(t0);
 
-    // softmax state of the dense score tasks (task t: query t / 16)
-    float m_run[STMAX], l_run[STMAX];
+    // softmax state and accumulator of head 4 rb + lgr (channel 16 nb + col)
+    float m_run[RBMAX], l_run[RBMAX];
+    float acc[RBMAX][NNB];
 #pragma unroll
-    for (int r = 0; r < STMAX; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
-    // dense accumulator: channel lane + 64 * r, query n
-    float acc[CPL_E][GMAX];
+    for (int rb = 0; rb < RBMAX; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.0f;
 #pragma unroll
-    for (int r = 0; r < CPL_E; ++r)
-#pragma unroll
-        for (int n = 0; n < GMAX; ++n) acc[r][n] = 0.0f;
-
-    CodeMagic<KB> kmagic;
-    CodeMagic<VB> vmagic;
-    kmagic.init();
-    vmagic.init();
+        for (int nb = 0; nb < NNB; ++nb) acc[rb][nb] = 0.0f;
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile, once
 
     for (int ti = t0; ti < t1; ++ti) {
         // ---- meta of the tile into the wave's LDS, then the next tile's meta ----
-        // (the K and V meta images are adjacent: chunk k lands at byte 16 k)
         static_assert(L::vmeta(0) == 16 * KC, "meta images must be adjacent");
 #pragma unroll
         for (int r = 0; r < MCH; ++r) {
@@ -454,200 +457,197 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         load_meta(ti + 1);
         wave_sync();
 
-        // ---- q' = qh * SK (hi/lo, scaled), zero-point term ----
+        // ---- q' = qh * SK as four 7-bit limbs, zero-point term, centring sums ----
 #pragma unroll
-        for (int r = 0; r < QTMAX; ++r) {
+        for (int r = 0; r < QR; ++r) {
             const int t = lane + 64 * r;
-            const int n = t / QT, rem = t % QT;
-            const int gq = rem / (NKB / 2), pr = rem % (NKB / 2);
-            const int r0 = run0_of<KB>(gq * (D / 4), 2 * pr), r1 = r0 + Codes<KB>::N / 2;
-            float qv[8];
+            if (GMAX > 4 && t >= 4 * RB * QPH) break;    // past the padded group (uniform)
+            const int n = t / QPH, rem = t % QPH;
+            const int gq = rem / (D / 16), rem2 = rem % (D / 16);
+            const int kc = rem2 >> 2, j = rem2 & 3;
+            float qv[4];
             float zt = 0.0f, mx = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ch = (e < 4 ? r0 : r1) + (e & 3);
+            for (int e = 0; e < 4; ++e) {
+                const int ch = gq * (D / 4) + 16 * kc + RunOrder<KB>::base(j) + RunOrder<KB>::kStride * e;
                 const float sk = h2f_bits(kmeta[ch]);
                 const float zk = h2f_bits(kmeta[D + ch]);
                 qv[e] = qh[r][e] * sk;
-                zt = __builtin_fmaf(qh[r][e], __builtin_fmaf(MK, sk, zk), zt);
+                zt = __builtin_fmaf(qh[r][e], __builtin_fmaf((float)MK, sk, zk), zt);
                 mx = fmaxf(mx, fabsf(qv[e]));
             }
-            zt = grp_sum<QT>(zt);
-            mx = grp_max<QT>(mx);
-            const float sq = pow2_scale(mx);
-            if (n < G) {
-                _Float16 hv[8], lv[8];
+            zt = grp_sum<QPH>(zt);
+            mx = grp_max<QPH>(mx);
+            const float sq = fx_scale(mx);
+            int hi[4], lo[4];
+            int shi = 0, slo = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    split_hi_lo(qv[e] * sq, hv[2 * e], lv[2 * e]);
-                    split_hi_lo(qv[4 + e] * sq, hv[2 * e + 1], lv[2 * e + 1]);
-                }
-                const int off = ((gq * G + n) * NKB + 2 * pr) * 8;
-                *reinterpret_cast<uint4*>(bqimg + off) = __builtin_bit_cast(uint4, hv);
-                *reinterpret_cast<uint4*>(bqimg + 32 * G * NKB + off) = __builtin_bit_cast(uint4, lv);
-                if (rem == 0) { st_qz[n] = zt; st_iq[n] = 1.0f / sq; }
+            for (int e = 0; e < 4; ++e) {
+                fx_split(qv[e], sq, hi[e], lo[e]);
+                shi += hi[e];
+                slo += lo[e];
+            }
+            shi = grp_isum<QPH>(shi);
+            slo = grp_isum<QPH>(slo);
+            uint32_t d[4];
+            limb_dwords(hi, lo, d);
+            // rows 4 (n % 4) + limb of run (gq, kc) in row block n / 4
+            uint8_t* dst = qaimg + (((n >> 2) * NKC + kc) * 4 + gq) * 256 + 4 * (n & 3) * 16 + 4 * j;
+#pragma unroll
+            for (int limb = 0; limb < 4; ++limb) *reinterpret_cast<uint32_t*>(dst + 16 * limb) = d[limb];
+            if (rem == 0) {
+                st_qz[n] = zt;
+                st_iq[n] = 1.0f / sq;
+                st_th[n] = MK * shi;
+                st_tl[n] = MK * slo;
             }
         }
         wave_sync();
-        // MFMA B operand: q' of head mrow; columns past the group repeat
-        // head G - 1 and their scores are never stored
-        h4_t bq_hi[NKB], bq_lo[NKB];
-        {
-            const int row = mrow < G ? mrow : G - 1;
-#pragma unroll
-            for (int k = 0; k < NKB; ++k) {
-                const int off = ((mgrp * G + row) * NKB + k) * 8;
-                bq_hi[k] = *reinterpret_cast<const h4_t*>(bqimg + off);
-                bq_lo[k] = *reinterpret_cast<const h4_t*>(bqimg + 32 * G * NKB + off);
-            }
-        }
 
-        // ---- scores: q.K^T on the matrix cores, per 16-token M-block ----
+        float s[RBMAX][TILE / 16];   // scores of head 4 rb + lgr, token tau(mb, col)
+        {
+            // ---- q.K^T: limb sums on the integer matrix cores ----
+            v4i_t qa[RBMAX][NKC];
 #pragma unroll
-        for (int mb = 0; mb < TILE / 16; ++mb) {
-            f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rb = 0; rb < RBMAX; ++rb) {
+                if (rb < RB) {
 #pragma unroll
-            for (int k = 0; k < NKB; k += 2) {
-                const h8_t av = cat8(code_operand<KB, KW>(kw[mb], k, kmagic),
-                                     code_operand<KB, KW>(kw[mb], k + 1, kmagic));
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cat8(bq_hi[k], bq_hi[k + 1]), c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cat8(bq_lo[k], bq_lo[k + 1]), c, 0, 0, 0);
+                    for (int kc = 0; kc < NKC; ++kc)
+                        qa[rb][kc] = *reinterpret_cast<const v4i_t*>(qaimg + (rb * NKC + kc) * 1024 + 16 * lane);
+                }
             }
-            if (mrow < G)
-                *reinterpret_cast<f4_t*>(sc + mrow * TILE + 16 * mb + 4 * mgrp) = c;
+            float qz[RBMAX], iq[RBMAX];
+            int th[RBMAX], tl[RBMAX];
+#pragma unroll
+            for (int rb = 0; rb < RBMAX; ++rb) {
+                const int h = rb < RB ? 4 * rb + lgr : 0;
+                qz[rb] = st_qz[h]; iq[rb] = st_iq[h]; th[rb] = st_th[h]; tl[rb] = st_tl[h];
+            }
+#pragma unroll
+            for (int mb = 0; mb < TILE / 16; ++mb) {
+                v4i_t kb[NKC];
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) kb[kc] = code_bytes<KB>(&kw[mb][KRW * kc]);
+                const float rk = h2f_bits(kmeta[2 * D + tok_r0<VB>(col) + tok_delta<VB>(mb)]);
+#pragma unroll
+                for (int rb = 0; rb < RBMAX; ++rb) {
+                    if (rb < RB) {
+                        v4i_t c = {0, 0, 0, 0};
+#pragma unroll
+                        for (int kc = 0; kc < NKC; ++kc)
+                            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[rb][kc], kb[kc], c, 0, 0, 0);
+                        s[rb][mb] = a.sm_scale * rk * __builtin_fmaf(limb_join(c, th[rb], tl[rb]), iq[rb], qz[rb]);
+                    }
+                }
+            }
         }
         load_k(ti + 1);
-        wave_sync();
 
-        // ---- online softmax, dense: task t = (query t/16, lane group, pair) ----
-#pragma unroll
-        for (int r = 0; r < STMAX; ++r) {
-            const int t = lane + 64 * r;
-            const int n = t / 16, rem = t % 16;
-            const int gv = rem / 4, pr = rem % 4;
-            const int r0 = run0_of<VB>(32 * gv, 2 * pr), r1 = r0 + Codes<VB>::N / 2;
-            const bool live = n < G;
-            const int nn = live ? n : 0;
-            const float iq = st_iq[nn], qz = st_qz[nn];
-            float s[8], svv[8], zvv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tok = (e < 4 ? r0 : r1) + (e & 3);
-                const float rk = h2f_bits(kmeta[2 * D + tok]);
-                svv[e] = h2f_bits(vmeta[tok]);
-                zvv[e] = h2f_bits(vmeta[TILE + tok]);
-                s[e] = a.sm_scale * rk * __builtin_fmaf(sc[nn * TILE + tok], iq, qz);
-            }
-            float mt = s[0], smax = 0.0f;
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) smax = fmaxf(smax, fabsf(svv[e]));
-            mt = grp_max<16>(mt);
-            smax = grp_max<16>(smax);
-            const float mnew = fmaxf(m_run[r], mt);
-            const float al = exp2f((m_run[r] - mnew) * kLog2e);
-            const float sp = pow2_scale(smax);
-            float p[8], lt = 0.0f, pz = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = exp2f((s[e] - mnew) * kLog2e);
-                lt += p[e];
-                pz = __builtin_fmaf(p[e], __builtin_fmaf(MV, svv[e], zvv[e]), pz);
-            }
-            lt = grp_sum<16>(lt);
-            pz = grp_sum<16>(pz);
-            m_run[r] = mnew;
-            l_run[r] = l_run[r] * al + lt;
-            if (live) {
-                _Float16 hv[8], lv[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    split_hi_lo(p[e] * svv[e] * sp, hv[2 * e], lv[2 * e]);
-                    split_hi_lo(p[4 + e] * svv[4 + e] * sp, hv[2 * e + 1], lv[2 * e + 1]);
-                }
-                const int off = ((gv * G + n) * NVB + 2 * pr) * 8;
-                *reinterpret_cast<uint4*>(paimg + off) = __builtin_bit_cast(uint4, hv);
-                *reinterpret_cast<uint4*>(paimg + 256 * G + off) = __builtin_bit_cast(uint4, lv);
-                if (rem == 0) {
-                    st_al[n] = al;
-                    st_pz[n] = pz;
-                    if (n == 0) st_ip[0] = 1.0f / sp;
-                }
-            }
-        }
-        wave_sync();
-        // MFMA A operand: p' of head mrow; rows past the group repeat head
-        // G - 1 and only rows of real heads are read back
-        h4_t pa_hi[NVB], pa_lo[NVB];
+        // ---- online softmax of head 4 rb + lgr over the tile; p' limbs into the image ----
+        float al[RBMAX], ip[RBMAX], pz[RBMAX];
+        int vth[RBMAX], vtl[RBMAX];
         {
-            const int row = mrow < G ? mrow : G - 1;
+            float sv[TILE / 16], zv[TILE / 16];
 #pragma unroll
-            for (int k = 0; k < NVB; ++k) {
-                const int off = ((mgrp * G + row) * NVB + k) * 8;
-                pa_hi[k] = *reinterpret_cast<const h4_t*>(paimg + off);
-                pa_lo[k] = *reinterpret_cast<const h4_t*>(paimg + 256 * G + off);
+            for (int mb = 0; mb < TILE / 16; ++mb) {
+                const int tok = tok_r0<VB>(col) + tok_delta<VB>(mb);
+                sv[mb] = h2f_bits(vmeta[tok]);
+                zv[mb] = h2f_bits(vmeta[TILE + tok]);
             }
-        }
-
-        // ---- p.V on the matrix cores, per 16-channel N-block ----
 #pragma unroll
-        for (int nb = 0; nb < NKB; ++nb) {
-            f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rb = 0; rb < RBMAX; ++rb) {
+                if (rb < RB) {
+                    float mt = s[rb][0];
 #pragma unroll
-            for (int k = 0; k < NVB; k += 2) {
-                const h8_t bv = cat8(code_operand<VB, VW>(vw[nb], k, vmagic),
-                                     code_operand<VB, VW>(vw[nb], k + 1, vmagic));
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(pa_hi[k], pa_hi[k + 1]), bv, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8(pa_lo[k], pa_lo[k + 1]), bv, c, 0, 0, 0);
-            }
-            if (4 * mgrp < G)
-                *reinterpret_cast<f4_t*>(pvc + (16 * nb + mrow) * GP + 4 * mgrp) = c;
-        }
-        load_v(ti + 1);
-        wave_sync();
-
-        // ---- dense update of the accumulator ----
-        {
-            const float ip = st_ip[0];
+                    for (int mb = 1; mb < TILE / 16; ++mb) mt = fmaxf(mt, s[rb][mb]);
+                    mt = grp_max<16>(mt);
+                    const float mnew = fmaxf(m_run[rb], mt);
+                    al[rb] = exp2f((m_run[rb] - mnew) * kLog2e);
+                    float p[TILE / 16], lt = 0.0f, pzs = 0.0f, mxp = 0.0f;
 #pragma unroll
-            for (int r = 0; r < CPL_E; ++r) {
-                const int ch = lane + 64 * r;
-                const float cv = h2f_bits(vmeta[2 * TILE + ch]);
+                    for (int mb = 0; mb < TILE / 16; ++mb) {
+                        p[mb] = exp2f((s[rb][mb] - mnew) * kLog2e);
+                        lt += p[mb];
+                        pzs = __builtin_fmaf(p[mb], __builtin_fmaf((float)MV, sv[mb], zv[mb]), pzs);
+                        p[mb] *= sv[mb];            // p' = p SV
+                        mxp = fmaxf(mxp, p[mb]);
+                    }
+                    lt = grp_sum<16>(lt);
+                    pz[rb] = grp_sum<16>(pzs);
+                    mxp = grp_max<16>(mxp);
+                    m_run[rb] = mnew;
+                    l_run[rb] = l_run[rb] * al[rb] + lt;
+                    const float sp = fx_scale(mxp);
+                    ip[rb] = 1.0f / sp;
+                    int hi[TILE / 16], lo[TILE / 16], shi = 0, slo = 0;
 #pragma unroll
-                for (int n = 0; n < GMAX; ++n) {
-                    if (n < G) {
-                        const float upd = cv * __builtin_fmaf(pvc[ch * GP + n], ip, st_pz[n]);
-                        acc[r][n] = __builtin_fmaf(acc[r][n], st_al[n], upd);
+                    for (int mb = 0; mb < TILE / 16; ++mb) {
+                        fx_split(p[mb], sp, hi[mb], lo[mb]);
+                        shi += hi[mb];
+                        slo += lo[mb];
+                    }
+                    vth[rb] = MV * grp_isum<16>(shi);
+                    vtl[rb] = MV * grp_isum<16>(slo);
+                    // run m of lane group col / 4, dword col % 4, rows 4 lgr + limb
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const int h4[4] = {hi[4 * m], hi[4 * m + 1], hi[4 * m + 2], hi[4 * m + 3]};
+                        const int l4[4] = {lo[4 * m], lo[4 * m + 1], lo[4 * m + 2], lo[4 * m + 3]};
+                        uint32_t d[4];
+                        limb_dwords(h4, l4, d);
+                        uint8_t* dst = paimg + ((rb * 2 + m) * 4 + (col >> 2)) * 256 + 4 * lgr * 16 + 4 * (col & 3);
+#pragma unroll
+                        for (int limb = 0; limb < 4; ++limb) *reinterpret_cast<uint32_t*>(dst + 16 * limb) = d[limb];
                     }
                 }
             }
         }
         wave_sync();
+
+        // ---- p.V: limb sums on the integer matrix cores, accumulator update ----
+        {
+            v4i_t pa[RBMAX][2];
+#pragma unroll
+            for (int rb = 0; rb < RBMAX; ++rb) {
+                if (rb < RB) {
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        pa[rb][m] = *reinterpret_cast<const v4i_t*>(paimg + (rb * 2 + m) * 1024 + 16 * lane);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb) {
+                const v4i_t vb0 = code_bytes<VB>(&vw[nb][0]);
+                const v4i_t vb1 = code_bytes<VB>(&vw[nb][VRW]);
+                const float cv = h2f_bits(vmeta[2 * TILE + 16 * nb + col]);
+#pragma unroll
+                for (int rb = 0; rb < RBMAX; ++rb) {
+                    if (rb < RB) {
+                        v4i_t c = {0, 0, 0, 0};
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[rb][0], vb0, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[rb][1], vb1, c, 0, 0, 0);
+                        const float upd = cv * __builtin_fmaf(limb_join(c, vth[rb], vtl[rb]), ip[rb], pz[rb]);
+                        acc[rb][nb] = __builtin_fmaf(acc[rb][nb], al[rb], upd);
+                    }
+                }
+            }
+        }
+        load_v(ti + 1);
+        wave_sync();
     }
 
     // ---- partial result of this split: (m, l, acc[D]) per query head ----
 #pragma unroll
-    for (int r = 0; r < CPL_E; ++r) {
-        const int ch = lane + 64 * r;
+    for (int rb = 0; rb < RBMAX; ++rb) {
+        const int n = 4 * rb + lgr;
+        if (rb < RB && n < G) {
+            float* p = a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
 #pragma unroll
-        for (int n = 0; n < GMAX; ++n) {
-            if (n < G) {
-                const int h = g * G + n;
-                float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_parts + split) * (D + 2);
-                p[2 + ch] = acc[r][n];
+            for (int nb = 0; nb < NNB; ++nb) p[2 + 16 * nb + col] = acc[rb][nb];
+            if (col == 0) {
+                p[0] = m_run[rb];
+                p[1] = l_run[rb];
             }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < STMAX; ++r) {
-        const int t = lane + 64 * r;
-        const int n = t / 16;
-        if (n < G && (t % 16) == 0) {
-            const int h = g * G + n;
-            float* p = a.ws + (((size_t)b * a.n_q_heads + h) * a.n_parts + split) * (D + 2);
-            p[0] = m_run[r];
-            p[1] = l_run[r];
         }
     }
 }
