@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int G = a.n_q_heads / a.n_kv_heads;
-    const int RB = (G + 3) >> 2;
+    const int RB = GMAX == 4 ? 1 : (G + 3) >> 2;   // row blocks in use (one below 5 heads)
     const int sgroups = (a.n_splits + wpb - 1) / wpb;
     const int bg = blockIdx.x / sgroups;
     const int split = (blockIdx.x % sgroups) * wpb + wave;
