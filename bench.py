@@ -280,9 +280,12 @@ def stream_reference(dev, units, reps=5):
     """Plain streaming kernels moving each stage's bytes per tile pair
     (libkvarn_streamref.so, built with the library): the rate this device
     delivers for that read/write mix, the reference for each stage's HBM
-    fraction beside the nominal 8 TB/s.  Best of a loop kernel and an
-    unrolled one (with plain and with nontemporal stores), each at three
-    persistent grid sizes."""
+    fraction beside the nominal 8 TB/s.  Best over kernel layouts (a loop
+    kernel; an unrolled one with plain or nontemporal stores; for the
+    dequantize mix also phased kernels that read 4 or 8 units before writing
+    them), each at three persistent grid sizes; `variants` keeps every
+    layout's best rate.  `fp16_write` is the dequantiser's output alone
+    (write-only, the same 4.3 GB)."""
     import ctypes
     import torch
 
@@ -298,32 +301,39 @@ def stream_reference(dev, units, reps=5):
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    mixes = {"quantize_mix": (big, small), "dequantize_mix": (small, big),
-             "packed_read": (small, 0), "fp16_read": (big, 0)}
+    layouts = {0: "loop", 1: "unrolled", 2: "unrolled_nt", 3: "phased_4", 4: "phased_8"}
+    mixes = {"quantize_mix": (big, small, (0, 1, 2)), "dequantize_mix": (small, big, (0, 1, 2, 3, 4)),
+             "packed_read": (small, 0, (0, 1)), "fp16_read": (big, 0, (0, 1)),
+             "fp16_write": (0, big, (1, 2))}
     out = {}
-    for name, (rq, wq) in mixes.items():
-        best = None
-        for per_cu, unrolled in ((4, 0), (8, 0), (16, 0), (4, 1), (8, 1), (16, 1),
-                                 (4, 2), (8, 2), (16, 2)):
-            def run():
-                st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, unrolled,
-                        sink.data_ptr(), stream)
-                if st != 0:
-                    raise RuntimeError("stream reference launch failed: %d" % st)
-            for _ in range(2):
-                run()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            best = ms if best is None else min(best, ms)
+    for name, (rq, wq, kinds) in mixes.items():
         nbytes = units * (rq + wq) * 16
-        out[name] = {"ms": round(best, 4), "GBps": round(nbytes / (best / 1e3) / 1e9, 1),
-                     "frac_of_peak": round(nbytes / (best / 1e3) / HBM_PEAK, 4)}
+        variants = {}
+        for unrolled in kinds:
+            best = None
+            for per_cu in (4, 8, 16):
+                def run():
+                    st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, unrolled,
+                            sink.data_ptr(), stream)
+                    if st != 0:
+                        raise RuntimeError("stream reference launch failed: %d" % st)
+                for _ in range(2):
+                    run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                best = ms if best is None else min(best, ms)
+            variants[layouts[unrolled]] = round(nbytes / (best / 1e3) / 1e9, 1)
+        top = max(variants, key=variants.get)
+        gbs = variants[top]
+        out[name] = {"ms": round(nbytes / (gbs * 1e9) * 1e3, 4), "GBps": gbs,
+                     "frac_of_peak": round(gbs * 1e9 / HBM_PEAK, 4), "best_layout": top,
+                     "variants_GBps": variants}
     del src, dst
     torch.cuda.empty_cache()
     return out

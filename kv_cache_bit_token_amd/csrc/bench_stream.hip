@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void stream_mix_fixed(const uint4* __restrict_
     uint4 acc = make_uint4(0u, 0u, 0u, 0u);
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
         const uint4* s = src + u * RQ;
-        uint4 v[RL];
+        uint4 v[RL > 0 ? RL : 1];
 #pragma unroll
         for (int k = 0; k < RL; ++k) {
             const int i = threadIdx.x + 256 * k;
@@ -70,6 +70,43 @@ __global__ __launch_bounds__(256) void stream_mix_fixed(const uint4* __restrict_
         }
     }
     if (WQ == 0 && (acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[threadIdx.x] = acc.x;
+}
+
+// Phased variant: each workgroup reads the words of NB units (all loads in
+// flight together), then writes the NB units' outputs with nontemporal
+// stores, so every workgroup alternates long read and write bursts instead
+// of interleaving them unit by unit.
+template <int RQ, int WQ, int NB>
+__global__ __launch_bounds__(256) void stream_mix_phased(const uint4* __restrict__ src,
+                                                         uint4* __restrict__ dst, int64_t units,
+                                                         uint32_t* sink) {
+    constexpr int RL = (NB * RQ + 255) / 256, WL = (WQ + 255) / 256;
+    using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t u0 = (int64_t)blockIdx.x * NB; u0 < units; u0 += (int64_t)gridDim.x * NB) {
+        const int nb = (int)((units - u0) < NB ? (units - u0) : NB);
+        const uint4* s = src + u0 * RQ;
+        uint4 v[RL];
+#pragma unroll
+        for (int k = 0; k < RL; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            v[k] = (i < nb * RQ) ? s[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < RL; ++k) { acc.x ^= v[k].x; acc.y ^= v[k].y; acc.z ^= v[k].z; acc.w ^= v[k].w; }
+        for (int un = 0; un < nb; ++un) {
+            uint4* d = dst + (u0 + un) * WQ;
+#pragma unroll
+            for (int k = 0; k < WL; ++k) {
+                const int i = threadIdx.x + 256 * k;
+                if (i < WQ) {
+                    const u32x4 w = {acc.x ^ (uint32_t)i, acc.y ^ (uint32_t)un, acc.z, acc.w};
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(d + i));
+                }
+            }
+        }
+    }
+    if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[threadIdx.x] = acc.x;
 }
 
 // Vector-ALU reference: eight independent fp32 multiply-add chains per
@@ -195,7 +232,8 @@ extern "C" int kvarn_valu_class_reference(int32_t cls, void* out, int32_t blocks
 // Streams `units` units through a persistent grid of `blocks` workgroups of
 // 256 threads; with `unrolled` 1 (2: nontemporal stores), the tile-pair
 // mixes at head_dim 128 use the compile-time kernels (others fall back to the
-// loop kernel).  src holds units * rq words, dst units * wq words, sink 256
+// loop kernel); `unrolled` 3 / 4 run the dequantize mix phased, 4 / 8 units
+// read before their writes.  src holds units * rq words, dst units * wq words, sink 256
 // words; device pointers, 16-byte aligned.  Returns the hipError_t of the
 // launch (0 on success).
 extern "C" int kvarn_stream_reference(const void* src, void* dst, int64_t units, int32_t rq,
@@ -218,10 +256,21 @@ extern "C" int kvarn_stream_reference(const void* src, void* dst, int64_t units,
                                dim3(256), 0, st, s4, d4, units, k4);                            \
         return (int)hipGetLastError();                                                          \
     }
+    if (unrolled >= 3 && rq == 864 && wq == 4096) {
+        if (unrolled == 3)
+            hipLaunchKernelGGL((stream_mix_phased<864, 4096, 4>), dim3((unsigned)blocks), dim3(256),
+                               0, st, s4, d4, units, k4);
+        else
+            hipLaunchKernelGGL((stream_mix_phased<864, 4096, 8>), dim3((unsigned)blocks), dim3(256),
+                               0, st, s4, d4, units, k4);
+        return (int)hipGetLastError();
+    }
+    if (unrolled >= 3) return 1;
     KVARN_FIXED(4096, 864)
     KVARN_FIXED(864, 4096)
     KVARN_FIXED(864, 0)
     KVARN_FIXED(4096, 0)
+    KVARN_FIXED(0, 4096)
 #undef KVARN_FIXED
     hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
