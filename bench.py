@@ -34,7 +34,7 @@ By default the other workloads run too, kernel by kernel (dequantize
 256 x 8 x 8192, the head_dim sweep, attention 64 x 8 x 32768 and its fp16
 baseline), each with its own roofline entries.
 
-Prints one JSON line.  `--gpus` above 1 exits: this build runs on one GPU.
+Prints one JSON line.  `--gpus` above 1 exits: the benchmark runs on one GPU.
 `--copy-calibration` instead runs a plain 1 GiB device copy (the reference
 for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
@@ -73,8 +73,13 @@ def quant_ops_per_elem(D, n_iters):
 # (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
 # each with the SHA-256 prefix of the kernel's sources it was taken for.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295697942,
-                              "write_bytes": 906057504},
+    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295707491,
+                              "write_bytes": 906071859},
+    ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 981305862,
+                                "write_bytes": 4294979584},
+    # query rotation + split partials + combine
+    ("decode_attention", "prefill"): {"source_sha256": "057ee6452ba51a16", "fetch_bytes": 927988851,
+                                      "write_bytes": 19137126},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {
@@ -592,7 +597,7 @@ def main():
         print(json.dumps(alu_classes(torch.device("cuda:0"))), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the KVarN path on one GPU only; "
+        print("bench.py: the KVarN path is benchmarked on one GPU only; "
               "--gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

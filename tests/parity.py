@@ -20,8 +20,8 @@ kappa bounds the first-order change of o when every score's dot product
 carries an absolute error of one fp32 unit of its terms' magnitude
 (sm_scale |q| |k_t| by Cauchy-Schwarz, in any orthonormal basis, so for
 the rotated-domain kernel too); 16 units cover the score's roundings (the
-matrix-core accumulation steps, the fp16 hi/lo operand split, the scale
-products).  Where two tokens of very different value nearly tie for the
+fixed-point rounding of the query-side operand to 27 bits per head and
+tile, the join of the exact integer limb sums, the scale products).  Where two tokens of very different value nearly tie for the
 largest score, fp32 scores alone move o by more than 2e-3
 (tests/test_oracle_dequant_attention.py shows it on the decode-attention
 workload), so an fp32 kernel cannot meet a bare 2e-3 there.  The number of
