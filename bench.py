@@ -78,8 +78,8 @@ TRAFFIC = {
     ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 981305862,
                                 "write_bytes": 4294979584},
     # query rotation + split partials + combine
-    ("decode_attention", "prefill"): {"source_sha256": "057ee6452ba51a16", "fetch_bytes": 927988851,
-                                      "write_bytes": 19137126},
+    ("decode_attention", "prefill"): {"source_sha256": "69f6b1cc985afb8b", "fetch_bytes": 922671133,
+                                      "write_bytes": 14955136},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

@@ -17,19 +17,22 @@
 // minimum, so the uncentred terms would be large and of opposite sign).
 //
 // Integer matrix cores.  Both code contractions run on
-// v_mfma_i32_16x16x64_i8 with the codes as they are (bytes 0 .. 2^b - 1) on
-// one side and the other factor, q' = qh SK per head (or p' = p SV), as a
-// fixed-point integer X = rint(q' 2^f), |X| < 2^27 (2^f a power of two per
-// head and tile), split into four 7-bit limbs X = L3 2^21 + L2 2^14 + L1 2^7
-// + L0 on the other.  The 16 rows of that operand are 4 query heads x 4
-// limbs, so one instruction gives every lane the four limb sums of one
-// (head, token) score or (head, channel) output: exact int32 sums, centred
-// by subtracting mk * sum X (exact, in integers), joined as
-// (L3 2^7 + L2 part) 2^14 + (L1 2^7 + L0 part) with one fp32 rounding.
-//   q.K^T : A = q' limbs (4 heads x 4 limbs) x 64 channels, B = K code bytes
-//           (64 channels x 16 tokens), C = limb sums [head, limb][token];
-//   p.V   : A = p' limbs (4 heads x 4 limbs) x 64 tokens, B = V code bytes
-//           (64 tokens x 16 channels), C = limb sums [head, limb][channel].
+// v_mfma_i32_16x16x64_i8.  The codes enter centred and scaled, as signed
+// bytes 2^(8-b) (code - 2^(b-1)) (b = k_bits or v_bits), which the unpack
+// forms at no extra cost: shift the b-bit field to the top of its byte,
+// flip its top bit, mask.  The other factor, q' = qh SK per head (or
+// p' = p SV), is a fixed-point integer X = rint(q' 2^f), |X| < 2^30 (2^f a
+// power of two per head and tile), written as four signed base-256 digits
+// X = B3 2^24 + B2 2^16 + B1 2^8 + B0, B_i in [-128, 127]: the bytes of
+// (X + 0x808080) ^ 0x808080.  The 16 rows of that operand are 4 query heads
+// x 4 digits, so one instruction gives every lane the four exact int32
+// digit sums of one (head, token) score or (head, channel) output, already
+// centred; they are joined as (C3 2^8 + C2) 2^16 + (C1 2^8 + C0) with one
+// rounding to fp32 (and one exact power-of-two rescale).
+//   q.K^T : A = q' digits (4 heads x 4 digits) x 64 channels, B = K code
+//           bytes (64 channels x 16 tokens), C = digit sums [head, digit][token];
+//   p.V   : A = p' digits (4 heads x 4 digits) x 64 tokens, B = V code bytes
+//           (64 tokens x 16 channels), C = digit sums [head, digit][channel].
 // A lane (row / column l % 16, k-group l / 16) holds 16 bytes of a run of
 // 16 contraction indices; the byte order inside a run follows the cheapest
 // unpack of the packed codes (RunOrder), and the other operand follows it.
@@ -58,7 +61,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTargetWaves = 8192;   // splits in flight: 8 waves per SIMD on 256 CUs
+constexpr int kTargetWaves = 6144;   // splits: two rounds of 3 resident waves on each of the 1024 SIMDs
 constexpr float kLog2e = 1.4426950408889634f;
 
 void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
@@ -90,11 +93,11 @@ size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_p
     return qrot_offset(batch, n_q_heads, D, n_parts) + (size_t)batch * n_q_heads * D * sizeof(float);
 }
 
-// ---- packed codes -> bytes for the int8 matrix cores -----------------------
+// ---- packed codes -> centred bytes for the int8 matrix cores ----------------
 // One run of 16 codes (the 16 contraction indices one lane group gives one
-// instruction) becomes 4 dwords of bytes.
-//   4 bits (two packed dwords w0, w1):  dword 2q + h = (w_q >> 4h) & 0x0F0F0F0F
-//   2 bits (one packed dword w):         dword s      = (w >> 2s) & 0x03030303
+// instruction) becomes 4 dwords of signed bytes 2^(8-B) (c - 2^(B-1)):
+//   4 bits (two packed dwords w0, w1):  dword 2q + h holds nibble h of each byte of w_q
+//   2 bits (one packed dword w):         dword s      holds crumb s of each byte of w
 // so byte n of dword j holds run position base(j) + stride * n.
 template <int B> struct RunOrder;
 template <> struct RunOrder<4> {
@@ -108,14 +111,22 @@ template <> struct RunOrder<2> {
     __host__ __device__ static constexpr int base(int j) { return j; }
 };
 
+// The B-bit field at bit P of every byte of w, moved to the top of its byte
+// with its top bit flipped: as a signed byte that is 2^(8-B) (c - 2^(B-1)).
+template <int B, int P>
+__device__ __forceinline__ int centred_field(uint32_t w) {
+    constexpr uint32_t kTop = B == 4 ? 0xF0F0F0F0u : 0xC0C0C0C0u;
+    return (int)(((w << (8 - B - P)) ^ 0x80808080u) & kTop);
+}
+
 template <int B>
 __device__ __forceinline__ v4i_t code_bytes(const uint32_t* w) {
     if constexpr (B == 4) {
-        return (v4i_t){(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
-                       (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
+        return (v4i_t){centred_field<4, 0>(w[0]), centred_field<4, 4>(w[0]),
+                       centred_field<4, 0>(w[1]), centred_field<4, 4>(w[1])};
     } else {
-        return (v4i_t){(int)(w[0] & 0x03030303u), (int)((w[0] >> 2) & 0x03030303u),
-                       (int)((w[0] >> 4) & 0x03030303u), (int)((w[0] >> 6) & 0x03030303u)};
+        return (v4i_t){centred_field<2, 0>(w[0]), centred_field<2, 2>(w[0]),
+                       centred_field<2, 4>(w[0]), centred_field<2, 6>(w[0])};
     }
 }
 
@@ -127,6 +138,11 @@ template <int VB>
 __device__ __forceinline__ int tok_r0(int c) { return 32 * (c >> 2) + RunOrder<VB>::base(c & 3); }
 template <int VB>
 __host__ __device__ constexpr int tok_delta(int mb) { return 16 * (mb >> 2) + RunOrder<VB>::kStride * (mb & 3); }
+
+// 2^x on the transcendental unit without the library's denormal-range
+// guard: results below 2^-126 (softmax weights e^-87 below the running
+// maximum) come out as zero instead of subnormal.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // reductions over aligned groups of W lanes (W = 8, 16, 32, 64)
 template <int W>
@@ -149,67 +165,49 @@ __device__ __forceinline__ float grp_max(float v) {
     if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32));
     return v;
 }
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
-}
-template <int W>
-__device__ __forceinline__ int grp_isum(int v) {
-    v += dpp_i<DPP_XOR1>(v);
-    v += dpp_i<DPP_XOR2>(v);
-    v += dpp_i<DPP_HMIR>(v);
-    if constexpr (W >= 16) v += dpp_i<DPP_ROR8>(v);
-    if constexpr (W >= 32) v += __shfl_xor(v, 16);
-    if constexpr (W >= 64) v += __shfl_xor(v, 32);
-    return v;
-}
-
-// power-of-two scale s with max * s in [2^26, 2^27) (1 for max == 0): the
-// fixed-point range of the four 7-bit limbs
+// power-of-two scale s with max * s in [2^29, 2^30) (1 for max == 0): the
+// fixed-point range of the four signed base-256 digits
 __device__ __forceinline__ float fx_scale(float mx) {
     if (!(mx > 0.0f)) return 1.0f;
     int e;
     (void)frexpf(mx, &e);          // mx = m * 2^e, m in [0.5, 1)
-    return ldexpf(1.0f, 27 - e);
+    return ldexpf(1.0f, 30 - e);
 }
 
-// x = rint(v * s), |x| < 2^27, as hi = x >> 14 = L3 2^7 + L2 and lo = x & 0x3FFF = L1 2^7 + L0
-__device__ __forceinline__ void fx_split(float v, float s, int& hi, int& lo) {
+// x = rint(v * s), |x| < 2^30, as its signed base-256 digits B0 .. B3 in
+// bytes 0 .. 3: adding 128 below each of the upper three digit positions
+// makes every lower byte hold B_i + 128, and flipping those bytes' top
+// bits gives B_i in two's complement (the top byte is B3 as it is).
+__device__ __forceinline__ uint32_t fx_digits(float v, float s) {
     const int x = (int)__builtin_rintf(v * s);
-    hi = x >> 14;
-    lo = x & 0x3FFF;
+    return ((uint32_t)x + 0x808080u) ^ 0x808080u;
 }
 
-// low bytes of a0 .. a3 -> bytes 0 .. 3 of one dword
-__device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
-    const uint32_t x = __builtin_amdgcn_perm((uint32_t)a1, (uint32_t)a0, 0x0c0c0400u);
-    const uint32_t y = __builtin_amdgcn_perm((uint32_t)a3, (uint32_t)a2, 0x04000c0cu);
-    return x | y;
+// 4 x 4 byte transpose: d[i] byte n = byte i of a[n] (digit i of value n).
+__device__ __forceinline__ void digit_dwords(const uint32_t (&a)[4], uint32_t (&d)[4]) {
+    const uint32_t t0 = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);   // a0.0 a1.0 a0.1 a1.1
+    const uint32_t t1 = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);   // a0.2 a1.2 a0.3 a1.3
+    const uint32_t u0 = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+    const uint32_t u1 = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+    d[0] = __builtin_amdgcn_perm(u0, t0, 0x05040100u);
+    d[1] = __builtin_amdgcn_perm(u0, t0, 0x07060302u);
+    d[2] = __builtin_amdgcn_perm(u1, t1, 0x05040100u);
+    d[3] = __builtin_amdgcn_perm(u1, t1, 0x07060302u);
 }
 
-// The four limb dwords (L0, L1, L2, L3; byte n = value n) of four split values.
-__device__ __forceinline__ void limb_dwords(const int (&hi)[4], const int (&lo)[4], uint32_t (&d)[4]) {
-    d[0] = pack4(lo[0] & 127, lo[1] & 127, lo[2] & 127, lo[3] & 127);
-    d[1] = pack4(lo[0] >> 7, lo[1] >> 7, lo[2] >> 7, lo[3] >> 7);
-    d[2] = pack4(hi[0] & 127, hi[1] & 127, hi[2] & 127, hi[3] & 127);
-    d[3] = pack4(hi[0] >> 7, hi[1] >> 7, hi[2] >> 7, hi[3] >> 7);
-}
-
-// Limb sums c[i] = sum L_i * code of one (head, index), centred by the exact
-// integer sums t_hi = mid * sum (x >> 14), t_lo = mid * sum (x & 0x3FFF):
-// sum x (code - mid) = ((c3 2^7 + c2) - t_hi) 2^14 + ((c1 2^7 + c0) - t_lo).
-__device__ __forceinline__ float limb_join(v4i_t c, int t_hi, int t_lo) {
-    const int hi = (c[3] << 7) + c[2] - t_hi;
-    const int lo = (c[1] << 7) + c[0] - t_lo;
-    return __builtin_fmaf((float)hi, 16384.0f, (float)lo);
+// Digit sums c[i] = sum B_i * centred code of one (head, index):
+// sum x (code - mid) 2^(8-b) = ((c3 2^8 + c2) 2^16 + (c1 2^8 + c0)).
+__device__ __forceinline__ float limb_join(v4i_t c) {
+    const int hi = (c[3] << 8) + c[2];
+    const int lo = (c[1] << 8) + c[0];
+    return __builtin_fmaf((float)hi, 65536.0f, (float)lo);
 }
 
 // Per-wave LDS layout (bytes), for GQA group size G (RB = ceil(G / 4) row
-// blocks of 4 heads): the tile's meta (K then V, adjacent), the q' limb
-// image [rb][kc][lane][16 B] and the p' limb image [rb][m][lane][16 B] (both
-// in the matrix-core operand layout, one 16-byte read per lane), and four
-// per-head scalars of the scores (zero-point term, 1 / scale, two centring
-// sums).
+// blocks of 4 heads): the tile's meta (K then V, adjacent), the q' digit
+// image [rb][kc][lane][16 B] and the p' digit image [rb][m][lane][16 B]
+// (both in the matrix-core operand layout, one 16-byte read per lane), and
+// two per-head scalars of the scores (zero-point term, 1 / scale).
 template <int D>
 struct AttnLds {
     static constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
@@ -220,7 +218,7 @@ struct AttnLds {
     __host__ __device__ static constexpr int qa(int) { return 2 * KMH + 2 * VMH; }
     __host__ __device__ static constexpr int pa(int G) { return qa(G) + rb(G) * NKC * 1024; }
     __host__ __device__ static constexpr int stats(int G) { return pa(G) + rb(G) * 2 * 1024; }
-    __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 16 * 4 * rb(G); }
+    __host__ __device__ static constexpr int bytes(int G) { return stats(G) + 8 * 4 * rb(G); }
 };
 
 // Natural-order Walsh-Hadamard transform of one D-vector held by one
@@ -326,9 +324,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     uint8_t* qaimg = lds + L::qa(G);
     uint8_t* paimg = lds + L::pa(G);
     float* st_qz = reinterpret_cast<float*>(lds + L::stats(G));   // [4 RB] zero-point term
-    float* st_iq = st_qz + 4 * RB;                                   // [4 RB] 1 / q' scale
-    int* st_th = reinterpret_cast<int*>(st_iq + 4 * RB);            // [4 RB] centring, hi part
-    int* st_tl = st_th + 4 * RB;                                     // [4 RB] centring, lo part
+    float* st_iq = st_qz + 4 * RB;                                   // [4 RB] 1 / (q' scale * code scale)
 
     const int col = lane & 15;      // matrix-core row / column of this lane
     const int lgr = lane >> 4;      // matrix-core lane group: head of a score or output tile
@@ -457,7 +453,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         load_meta(ti + 1);
         wave_sync();
 
-        // ---- q' = qh * SK as four 7-bit limbs, zero-point term, centring sums ----
+        // ---- q' = qh * SK as four signed base-256 digits, zero-point term ----
 #pragma unroll
         for (int r = 0; r < QR; ++r) {
             const int t = lane + 64 * r;
@@ -479,34 +475,24 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             zt = grp_sum<QPH>(zt);
             mx = grp_max<QPH>(mx);
             const float sq = fx_scale(mx);
-            int hi[4], lo[4];
-            int shi = 0, slo = 0;
+            uint32_t xd[4], d[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                fx_split(qv[e], sq, hi[e], lo[e]);
-                shi += hi[e];
-                slo += lo[e];
-            }
-            shi = grp_isum<QPH>(shi);
-            slo = grp_isum<QPH>(slo);
-            uint32_t d[4];
-            limb_dwords(hi, lo, d);
-            // rows 4 (n % 4) + limb of run (gq, kc) in row block n / 4
+            for (int e = 0; e < 4; ++e) xd[e] = fx_digits(qv[e], sq);
+            digit_dwords(xd, d);
+            // rows 4 (n % 4) + digit of run (gq, kc) in row block n / 4
             uint8_t* dst = qaimg + (((n >> 2) * NKC + kc) * 4 + gq) * 256 + 4 * (n & 3) * 16 + 4 * j;
 #pragma unroll
-            for (int limb = 0; limb < 4; ++limb) *reinterpret_cast<uint32_t*>(dst + 16 * limb) = d[limb];
+            for (int dg = 0; dg < 4; ++dg) *reinterpret_cast<uint32_t*>(dst + 16 * dg) = d[dg];
             if (rem == 0) {
                 st_qz[n] = zt;
-                st_iq[n] = 1.0f / sq;
-                st_th[n] = MK * shi;
-                st_tl[n] = MK * slo;
+                st_iq[n] = 1.0f / (sq * (float)(256 >> KB));   // the codes enter as 2^(8-KB) (c - MK)
             }
         }
         wave_sync();
 
         float s[RBMAX][TILE / 16];   // scores of head 4 rb + lgr, token tau(mb, col)
         {
-            // ---- q.K^T: limb sums on the integer matrix cores ----
+            // ---- q.K^T: digit sums on the integer matrix cores ----
             v4i_t qa[RBMAX][NKC];
 #pragma unroll
             for (int rb = 0; rb < RBMAX; ++rb) {
@@ -517,11 +503,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 }
             }
             float qz[RBMAX], iq[RBMAX];
-            int th[RBMAX], tl[RBMAX];
 #pragma unroll
             for (int rb = 0; rb < RBMAX; ++rb) {
                 const int h = rb < RB ? 4 * rb + lgr : 0;
-                qz[rb] = st_qz[h]; iq[rb] = st_iq[h]; th[rb] = st_th[h]; tl[rb] = st_tl[h];
+                qz[rb] = st_qz[h]; iq[rb] = st_iq[h];
             }
 #pragma unroll
             for (int mb = 0; mb < TILE / 16; ++mb) {
@@ -536,16 +521,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
                         for (int kc = 0; kc < NKC; ++kc)
                             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[rb][kc], kb[kc], c, 0, 0, 0);
-                        s[rb][mb] = a.sm_scale * rk * __builtin_fmaf(limb_join(c, th[rb], tl[rb]), iq[rb], qz[rb]);
+                        s[rb][mb] = a.sm_scale * rk * __builtin_fmaf(limb_join(c), iq[rb], qz[rb]);
                     }
                 }
             }
         }
         load_k(ti + 1);
 
-        // ---- online softmax of head 4 rb + lgr over the tile; p' limbs into the image ----
+        // ---- online softmax of head 4 rb + lgr over the tile; p' digits into the image ----
         float al[RBMAX], ip[RBMAX], pz[RBMAX];
-        int vth[RBMAX], vtl[RBMAX];
         {
             float sv[TILE / 16], zv[TILE / 16];
 #pragma unroll
@@ -562,11 +546,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                     for (int mb = 1; mb < TILE / 16; ++mb) mt = fmaxf(mt, s[rb][mb]);
                     mt = grp_max<16>(mt);
                     const float mnew = fmaxf(m_run[rb], mt);
-                    al[rb] = exp2f((m_run[rb] - mnew) * kLog2e);
+                    al[rb] = exp2_fast((m_run[rb] - mnew) * kLog2e);
                     float p[TILE / 16], lt = 0.0f, pzs = 0.0f, mxp = 0.0f;
 #pragma unroll
                     for (int mb = 0; mb < TILE / 16; ++mb) {
-                        p[mb] = exp2f((s[rb][mb] - mnew) * kLog2e);
+                        p[mb] = exp2_fast((s[rb][mb] - mnew) * kLog2e);
                         lt += p[mb];
                         pzs = __builtin_fmaf(p[mb], __builtin_fmaf((float)MV, sv[mb], zv[mb]), pzs);
                         p[mb] *= sv[mb];            // p' = p SV
@@ -578,33 +562,24 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                     m_run[rb] = mnew;
                     l_run[rb] = l_run[rb] * al[rb] + lt;
                     const float sp = fx_scale(mxp);
-                    ip[rb] = 1.0f / sp;
-                    int hi[TILE / 16], lo[TILE / 16], shi = 0, slo = 0;
-#pragma unroll
-                    for (int mb = 0; mb < TILE / 16; ++mb) {
-                        fx_split(p[mb], sp, hi[mb], lo[mb]);
-                        shi += hi[mb];
-                        slo += lo[mb];
-                    }
-                    vth[rb] = MV * grp_isum<16>(shi);
-                    vtl[rb] = MV * grp_isum<16>(slo);
-                    // run m of lane group col / 4, dword col % 4, rows 4 lgr + limb
+                    ip[rb] = 1.0f / (sp * (float)(256 >> VB));   // the codes enter as 2^(8-VB) (c - MV)
+                    // run m of lane group col / 4, dword col % 4, rows 4 lgr + digit
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {
-                        const int h4[4] = {hi[4 * m], hi[4 * m + 1], hi[4 * m + 2], hi[4 * m + 3]};
-                        const int l4[4] = {lo[4 * m], lo[4 * m + 1], lo[4 * m + 2], lo[4 * m + 3]};
-                        uint32_t d[4];
-                        limb_dwords(h4, l4, d);
+                        uint32_t xd[4], d[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xd[e] = fx_digits(p[4 * m + e], sp);
+                        digit_dwords(xd, d);
                         uint8_t* dst = paimg + ((rb * 2 + m) * 4 + (col >> 2)) * 256 + 4 * lgr * 16 + 4 * (col & 3);
 #pragma unroll
-                        for (int limb = 0; limb < 4; ++limb) *reinterpret_cast<uint32_t*>(dst + 16 * limb) = d[limb];
+                        for (int dg = 0; dg < 4; ++dg) *reinterpret_cast<uint32_t*>(dst + 16 * dg) = d[dg];
                     }
                 }
             }
         }
         wave_sync();
 
-        // ---- p.V: limb sums on the integer matrix cores, accumulator update ----
+        // ---- p.V: digit sums on the integer matrix cores, accumulator update ----
         {
             v4i_t pa[RBMAX][2];
 #pragma unroll
@@ -626,7 +601,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                         v4i_t c = {0, 0, 0, 0};
                         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[rb][0], vb0, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[rb][1], vb1, c, 0, 0, 0);
-                        const float upd = cv * __builtin_fmaf(limb_join(c, vth[rb], vtl[rb]), ip[rb], pz[rb]);
+                        const float upd = cv * __builtin_fmaf(limb_join(c), ip[rb], pz[rb]);
                         acc[rb][nb] = __builtin_fmaf(acc[rb][nb], al[rb], upd);
                     }
                 }
