@@ -640,25 +640,35 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int s = lane; s < a.n_parts; s += 64) M = fmaxf(M, p[(size_t)s * (D + 2)]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    // the normaliser and the weighted sum of the parts' accumulators, CPL
+    // channels per lane.  In each chunk of 64 parts, lane k computes part
+    // k's weight and the loop reads it back lane by lane, so that the
+    // accumulator loads of successive parts do not wait on one another.
     float L = 0.0f;
-    for (int s = lane; s < a.n_parts; s += 64) {
-        const float ms = p[(size_t)s * (D + 2)];
-        if (ms != -INFINITY) L += p[(size_t)s * (D + 2) + 1] * exp2f((ms - M) * kLog2e);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    // weighted sum of the parts' accumulators, CPL channels per lane
     float v[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) v[c] = 0.0f;
-    for (int s = 0; s < a.n_parts; ++s) {
-        const float* ps = p + (size_t)s * (D + 2);
-        const float ms = ps[0];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f((ms - M) * kLog2e);
+    for (int base = 0; base < a.n_parts; base += 64) {
+        const int s = base + lane;
+        float w = 0.0f;
+        if (s < a.n_parts) {
+            const float ms = p[(size_t)s * (D + 2)];
+            if (ms != -INFINITY) {
+                w = exp2f((ms - M) * kLog2e);
+                L += p[(size_t)s * (D + 2) + 1] * w;
+            }
+        }
+        const int cnt = min(64, a.n_parts - base);
+        const float* pb = p + (size_t)base * (D + 2) + 2 + CPL * lane;
+#pragma unroll 4
+        for (int k = 0; k < cnt; ++k) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(ps[2 + CPL * lane + c], w, v[c]);
+            for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(pb[(size_t)k * (D + 2) + c], wk, v[c]);
+        }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     const float il = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) v[c] *= il;
