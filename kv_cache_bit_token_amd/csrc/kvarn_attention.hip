@@ -275,6 +275,9 @@ __global__ __launch_bounds__(256) void attn_rotate_q_kernel(AttnArgs a) {
     for (int c = 0; c < CPL; ++c) a.qrot[(size_t)bh * D + CPL * lane + c] = v[c];
 }
 
+template <int D, int GM>
+__device__ void attn_tail_block(const AttnArgs& a, int bg, uint8_t* lds);
+
 template <int D, int KB, int VB, int GMAX>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     using L = AttnLds<D>;
@@ -299,6 +302,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int G = a.n_q_heads / a.n_kv_heads;
     const int RB = GMAX == 4 ? 1 : (G + 3) >> 2;   // row blocks in use (one below 5 heads)
     const int sgroups = (a.n_splits + wpb - 1) / wpb;
+    if (a.tail_in_grid) {
+        // the fp16 tails, one 256-thread block per (b, KV head), after the splits' blocks
+        const int pblocks = a.batch * a.n_kv_heads * sgroups;
+        if ((int)blockIdx.x >= pblocks) {
+            attn_tail_block<D, GMAX>(a, (int)blockIdx.x - pblocks, smem);
+            return;
+        }
+    }
     const int bg = blockIdx.x / sgroups;
     const int split = (blockIdx.x % sgroups) * wpb + wave;
     if (split >= a.n_splits) return;
@@ -693,21 +704,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 //   p . V:  thread (s, c) sums tokens s, s + NS, ... over channel chunk c
 //           (8 channels, one 16-byte load per token); the NS token slices
 //           are reduced across lanes, then across the four waves in LDS.
+// LDS of one tail workgroup: q (then the summed acc) [GM][D], p [TILE][GM],
+// per-wave max and sum [2][4][GM], final m and l [2][GM].
 template <int D, int GM>
-__global__ __launch_bounds__(256) void attn_tail_kernel(AttnArgs a) {
+struct TailLds {
+    static constexpr int kBytes = 4 * (GM * D + TILE * GM + 8 * GM + 2 * GM);
+};
+
+// The tail of (b, KV head) bg, by one 256-thread workgroup (lds: TailLds
+// bytes, 16-byte aligned).
+template <int D, int GM>
+__device__ void attn_tail_block(const AttnArgs& a, int bg, uint8_t* lds) {
     constexpr int NT = 256;
     constexpr int HC = D / 2;                      // channels per score thread
     constexpr int CPR = D / 8;                     // 16-byte chunks of a padded row
     constexpr int NS = NT / CPR;                   // token slices of the p . V phase
     constexpr int TPS = TILE / NS;                 // tokens per slice
     constexpr int SPW = 64 / CPR;                  // slices per wave
-    __shared__ __align__(16) float qs[GM * D];     // q; then the summed acc
-    __shared__ __align__(16) float ps[TILE * GM];  // p[t][n]
-    __shared__ float red[2][4][GM];                // per-wave max and sum
-    __shared__ float ml[2][GM];                    // final m and l
+    float* qs = reinterpret_cast<float*>(lds);     // q; then the summed acc
+    float* ps = qs + GM * D;                       // p[t][n]
+    float (*red)[4][GM] = reinterpret_cast<float (*)[4][GM]>(ps + TILE * GM);   // per-wave max and sum
+    float (*ml)[GM] = reinterpret_cast<float (*)[GM]>(ps + TILE * GM + 8 * GM); // final m and l
     float* os = qs;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int bg = blockIdx.x;
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int G = a.n_q_heads / a.n_kv_heads;
     const int d0 = a.d0;
@@ -847,6 +866,14 @@ __global__ __launch_bounds__(256) void attn_tail_kernel(AttnArgs a) {
     }
 }
 
+// One workgroup per (b, KV head), when the tails are not run by the partial
+// kernel's grid.
+template <int D, int GM>
+__global__ __launch_bounds__(256) void attn_tail_kernel(AttnArgs a) {
+    __shared__ __align__(16) uint8_t lds[TailLds<D, GM>::kBytes];
+    attn_tail_block<D, GM>(a, blockIdx.x, lds);
+}
+
 __global__ void fill_zero_kernel(float* out, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = 0.0f;
@@ -869,13 +896,20 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
         if (wpb > 4) wpb = 4;
         if (wpb < 1) wpb = 1;
         const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
-        const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
+        int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
+        // A paged call's fp16 tails run as extra blocks of the same grid where
+        // those blocks have the tail's 256 threads and its LDS, so they overlap
+        // the splits instead of following them.
+        if (a.tail_len && wpb == 4 && TailLds<D, GMAX>::kBytes <= per_wave * wpb) {
+            a.tail_in_grid = 1;
+            blocks += (int64_t)a.batch * a.n_kv_heads;
+        }
         hipLaunchKernelGGL((attn_partial_kernel<D, KB, VB, GMAX>), dim3((unsigned)blocks),
                            dim3(64 * wpb), (size_t)per_wave * wpb, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.tail_len) {
+    if (a.tail_len && !a.tail_in_grid) {
         hipLaunchKernelGGL((attn_tail_kernel<D, GMAX>), dim3((unsigned)(a.batch * a.n_kv_heads)),
                            dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();

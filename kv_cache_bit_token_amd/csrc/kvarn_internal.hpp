@@ -59,6 +59,7 @@ struct AttnArgs {
     const int32_t* tail_len = nullptr;  // [batch] fp16 tail tokens
     const uint16_t* k_tail = nullptr;   // [batch][n_kv_heads][128][d0]
     const uint16_t* v_tail = nullptr;
+    int tail_in_grid = 0;               // set by the launcher: tails run as extra partial-kernel blocks
     int64_t pool_blocks = 0;
     float* qrot = nullptr;              // [B][Hq][D] rotated queries (set by the launcher)
 };
