@@ -73,13 +73,13 @@ def quant_ops_per_elem(D, n_iters):
 # (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
 # each with the SHA-256 prefix of the kernel's sources it was taken for.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295707491,
-                              "write_bytes": 906071859},
-    ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 981305862,
-                                "write_bytes": 4294979584},
+    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295724054,
+                              "write_bytes": 906053472},
+    ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 924491478,
+                                "write_bytes": 4294990976},
     # query rotation + split partials + combine
-    ("decode_attention", "prefill"): {"source_sha256": "69f6b1cc985afb8b", "fetch_bytes": 922671133,
-                                      "write_bytes": 14955136},
+    ("decode_attention", "prefill"): {"source_sha256": "f69675975ac41b27", "fetch_bytes": 922682888,
+                                      "write_bytes": 14953056},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

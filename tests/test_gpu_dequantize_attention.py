@@ -96,6 +96,19 @@ def test_attention_group_sizes_and_widths(B, n_kv, Hq, T, d0):
     print(compare_attention(out, ref))
 
 
+@pytest.mark.parametrize("B,n_kv,Hq,tiles,d0", [(1, 1, 4, 150, 128), (2, 1, 8, 100, 64)])
+def test_attention_more_than_64_splits(B, n_kv, Hq, tiles, d0):
+    """Few (sequence, KV head) pairs over many tiles: one tile per split, so
+    the combine kernel merges more than 64 splits per head and walks its
+    weights in several chunks of 64."""
+    wsb = kv.decode_attention_workspace(batch=B, n_q_heads=Hq, n_kv_heads=n_kv, tiles_per_seq=tiles,
+                                        head_dim=d0)
+    D = oracle.padded_dim(d0)
+    assert wsb >= B * Hq * 65 * (D + 2) * 4, "fewer than 65 splits: the case would not span two chunks"
+    out, ref = _attention_case(B, n_kv, Hq, tiles * 128, d0, seed=tiles + d0)
+    record("attention, more than 64 splits %s" % ((B, n_kv, Hq, tiles, d0),), compare_attention(out, ref))
+
+
 def test_attention_other_presets():
     for kb, vb in ((4, 4), (2, 2), (2, 4)):
         out, ref = _attention_case(1, 2, 8, 256, 128, seed=3, kb=kb, vb=vb)
