@@ -78,7 +78,7 @@ TRAFFIC = {
     ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 924491478,
                                 "write_bytes": 4294990976},
     # query rotation + split partials + combine
-    ("decode_attention", "prefill"): {"source_sha256": "f69675975ac41b27", "fetch_bytes": 922682888,
+    ("decode_attention", "prefill"): {"source_sha256": "591a44c69555628e", "fetch_bytes": 922682888,
                                       "write_bytes": 14953056},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")

@@ -46,19 +46,18 @@
 // are the meta, the q' image and the p' image.
 //
 // Work split: each wavefront owns one split (a run of tiles) of one
-// (b, KV head) and every query head of that head's GQA group; waves never
-// synchronise with each other.  A combine kernel merges the splits' (max,
-// sum, acc) and undoes the rotation.
+// (b, KV head) and every query head of that head's GQA group; these waves
+// never synchronise with each other.  A paged call's fp16 tails run as
+// extra 256-thread workgroups of the same grid where its workgroups have
+// 256 threads (they synchronise only among their own waves), else as a
+// kernel of their own.  A combine kernel merges the splits' (max, sum, acc)
+// and undoes the rotation.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 #include "kvarn_rsrc.hpp"
 
 namespace kvarn {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTargetWaves = 6144;   // splits: two rounds of 3 resident waves on each of the 1024 SIMDs
