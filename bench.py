@@ -72,14 +72,47 @@ def quant_ops_per_elem(D, n_iters):
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
 # each with the SHA-256 prefix of the kernel's sources it was taken for.
+# decode_attention sums the query rotation, the split partials and the
+# combine; fp16_decode_attention its partials and combine.
 TRAFFIC = {
     ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295724054,
                               "write_bytes": 906053472},
     ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 924491478,
                                 "write_bytes": 4294990976},
-    # query rotation + split partials + combine
     ("decode_attention", "prefill"): {"source_sha256": "591a44c69555628e", "fetch_bytes": 922682888,
                                       "write_bytes": 14953056},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 2454535953,
+                                              "write_bytes": 8590094348},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67465886,
+                                          "write_bytes": 14942208},
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 15141639,
+                                            "write_bytes": 67123744},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67464930,
+                                          "write_bytes": 14942208},
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 15141468,
+                                            "write_bytes": 67135691},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101036578,
+                                          "write_bytes": 28311552},
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 28567101,
+                                            "write_bytes": 100677173},
+    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101035183,
+                                          "write_bytes": 28311552},
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 28566760,
+                                            "write_bytes": 100678912},
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268844605,
+                                           "write_bytes": 55050861},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 57841212,
+                                             "write_bytes": 268481685},
+    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268842762,
+                                           "write_bytes": 55051102},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 57739412,
+                                             "write_bytes": 268505696},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "591a44c69555628e", "fetch_bytes": 1828609017,
+                                                          "write_bytes": 15108329},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 4714063900,
+                                           "write_bytes": 18111978},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 9293708088,
+                                                               "write_bytes": 18154938},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {
@@ -531,9 +564,12 @@ def config_sweep(kv, synthetic, dev, rooflines, reps=10):
             key = "head_dim_%d_iters_%d" % (d0, it)
             out[key] = {"padded": D, "quantize": rates(ms_q, fp16, fp16 + packed_b, n),
                         "dequantize": rates(ms_d, fp16, fp16 + packed_b, n)}
-            rooflines.append(hbm_roofline("quantize", key, ms_q, fp16 + packed_b))
-            rooflines.append(alu_roofline(key, ms_q, D, it, 2 * n * 128 * D))
-            rooflines.append(hbm_roofline("dequantize", key, ms_d, fp16 + packed_b))
+            rooflines.append(hbm_roofline("quantize", key, ms_q, fp16 + packed_b,
+                                          measured_traffic("quantize", key)))
+            rooflines.append(alu_roofline(key, ms_q, D, it, 2 * n * 128 * D,
+                                          measured_traffic("quantize", key)))
+            rooflines.append(hbm_roofline("dequantize", key, ms_d, fp16 + packed_b,
+                                          measured_traffic("dequantize", key)))
             del outs
         del k, v, kt, vt, ins
         torch.cuda.empty_cache()
