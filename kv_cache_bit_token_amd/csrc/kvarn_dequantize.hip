@@ -13,12 +13,17 @@
 // the quantiser (kvarn_device.hpp).  A workgroup walks a strided sequence of
 // tiles (K tiles or V tiles) and loads the packed codes and meta of the next
 // tile into registers while it transforms the current one, so the HBM
-// latency of the (small) packed input overlaps the arithmetic.  Each lane
-// reads exactly the bytes it needs: K codes are token-major, so a lane's 16
-// channels of one token are one 8- (4-bit) or 4-byte (2-bit) word; V codes
-// are channel-major, so lanes holding neighbouring token groups load whole
-// words of their channel rows and swap bytes through LDS inside the
-// wavefront.  The per-token K factor RK_t and the 1/sqrt(D) scale are applied
+// latency of the (small) packed input overlaps the arithmetic.  K codes are
+// token-major, so a lane's 16 channels of one token are one 8- (4-bit) or
+// 4-byte (2-bit) word, read by that lane alone.  V codes are channel-major:
+// a wavefront's tokens are a few bytes of every channel row, so the
+// workgroup reads the tile's whole code block once, each wavefront 1 KB of
+// consecutive bytes per load, and passes it through LDS; lanes holding
+// neighbouring token groups then take whole words of their channel rows and
+// swap bytes inside the wavefront.  (Read by each wavefront straight from
+// memory, the partly used 128-byte lines of the V rows were fetched from HBM
+// again when the cache dropped them between the wavefronts' reads.)  The
+// per-token K factor RK_t and the 1/sqrt(D) scale are applied
 // after the transform (they commute with it); for V, 1/sqrt(D) is folded
 // into CV_j.
 #include "kvarn_device.hpp"
@@ -59,8 +64,37 @@ template <int D, int BITS> struct Packed<D, BITS, true> {
     uint4 m[MetaPlan<D, true>::NS];      // meta chunks
 };
 template <int D, int BITS> struct Packed<D, BITS, false> {
-    uint32_t g[BITS == 2 ? 4 : 8];       // words of channel rows (before the in-wave swap)
+    uint4 v[BITS / 2];                   // this thread's 16-byte pieces of the tile's code block
     uint4 m[MetaPlan<D, false>::NS];
+};
+
+// Word (channel row r, word w) of a V tile's code block in the workgroup's
+// LDS copy.  Rows are 4 * VB words long; with L = log2(D):
+//   2-bit: 16-byte word G holds word w of rows 4 (r >> 2) .. 4 (r >> 2) + 3,
+//          G = (r >> 2 | w << (L - 2)) ^ (r >> 6) << (8 - L) ^ (w >> 2 & 1) << 2;
+//   4-bit: 16-byte word G + 2 D ((r >> 3) & 1) holds word w of the four rows
+//          that differ in bits 1 and 2 of r,
+//          G = (r & 1 | (r >> 4) << 1 | w << (L - 3)) ^ (w >> 2 & 3) << 1 ^ (r >> 7).
+// A lane's rows 16 nb + 4 j + n (2-bit) or 16 nb + 2 q + j (4-bit) of its
+// word m are then one or two aligned 16-byte words, the 16-byte reads of a
+// quarter wave and the 4-byte stores of a half wave (the stored pieces are
+// 16 consecutive bytes of one row each) fall on distinct banks at every
+// head_dim, and word w + i of a row sits i * VQ words after word w
+// (w % 4 == 0, i < 4).
+template <int D, int BITS>
+struct VBlock {
+    static constexpr int L = D == 64 ? 6 : D == 128 ? 7 : 8;
+    static constexpr int WORDS = 4 * BITS * D;         // words of one tile's code block
+    static constexpr int VQ = BITS == 2 ? D : D / 2;   // word step of w -> w + 1 (w % 4 < 3)
+    __device__ static int addr(int r, int w) {
+        if constexpr (BITS == 2) {
+            const int G = ((r >> 2) | (w << (L - 2))) ^ ((r >> 6) << (8 - L)) ^ (((w >> 2) & 1) << 2);
+            return 4 * G + (r & 3);
+        } else {
+            const int G = ((r & 1) | ((r >> 4) << 1) | (w << (L - 3))) ^ (((w >> 2) & 3) << 1) ^ (r >> 7);
+            return 4 * (G + 2 * D * ((r >> 3) & 1)) + ((r >> 1) & 3);
+        }
+    }
 };
 
 __device__ __forceinline__ float half_of(const uint32_t* pairs, int k) {
@@ -98,24 +132,18 @@ __device__ __forceinline__ void load_tile(Packed<D, BITS, IS_K>& p, const uint8_
             }
         }
     } else {
-        constexpr int ROWB = TILE * BITS / 8;   // bytes per channel row
-        if constexpr (BITS == 2) {
-            const int m = tb >> 2, j = tb & 3;
+        // the tile's code block, 16 bytes per thread and load: each wave reads
+        // 1 KB of consecutive bytes
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-                p.g[n] = *reinterpret_cast<const uint32_t*>(codes + (16 * nb + 4 * j + n) * ROWB + 4 * m);
-        } else {
-            const int m = tb >> 1, j = tb & 1;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                p.g[q] = *reinterpret_cast<const uint32_t*>(codes + (16 * nb + 2 * q + j) * ROWB + 4 * m);
-        }
+        for (int k = 0; k < BITS / 2; ++k)
+            p.v[k] = reinterpret_cast<const uint4*>(codes)[threadIdx.x + 2 * D * k];
     }
 }
 
 template <int D, int BITS, bool IS_K, bool FULL>
 __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, int d0,
-                                                uint16_t* __restrict__ out, uint32_t* xch) {
+                                                uint16_t* __restrict__ out, uint32_t* xch,
+                                                uint32_t* vb) {
     constexpr int R = D / CPL;
     constexpr uint32_t MASK = (1u << BITS) - 1;
     using N = Net<R>;
@@ -157,15 +185,44 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
             }
         }
     } else {
+        // The code block through LDS: every thread stores its 16-byte pieces
+        // (channel row r, words w0 .. w0 + 3), then lane (tb, nb) reads word
+        // m of the rows it swaps below, g[n] = row 16 nb + 4 j + n (2-bit,
+        // m = tb / 4, j = tb % 4) or g[q] = row 16 nb + 2 q + j (4-bit,
+        // m = tb / 2, j = tb % 2).  vb alternates between two buffers from
+        // tile to tile, so one barrier per tile orders the stores after the
+        // reads of two tiles back.
+        using VBk = VBlock<D, BITS>;
+        uint32_t g[BITS == 2 ? 4 : 8];
+#pragma unroll
+        for (int k = 0; k < BITS / 2; ++k) {
+            const int P = tid + 2 * D * k;   // 16-byte piece of the block
+            const int a0 = BITS == 2 ? VBk::addr(P >> 1, 4 * (P & 1)) : VBk::addr(P >> 2, 4 * (P & 3));
+            vb[a0] = p.v[k].x;
+            vb[a0 + VBk::VQ] = p.v[k].y;
+            vb[a0 + 2 * VBk::VQ] = p.v[k].z;
+            vb[a0 + 3 * VBk::VQ] = p.v[k].w;
+        }
+        __syncthreads();
+        if constexpr (BITS == 2) {
+            const uint4 a = *reinterpret_cast<const uint4*>(vb + VBk::addr(16 * nb + 4 * (tb & 3), tb >> 2));
+            g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+        } else {
+            const uint4 a = *reinterpret_cast<const uint4*>(vb + VBk::addr(16 * nb + (tb & 1), tb >> 1));
+            const uint4 b = *reinterpret_cast<const uint4*>(vb + VBk::addr(16 * nb + 8 + (tb & 1), tb >> 1));
+            g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+            g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+        }
+
         // in-wave swap: lane (token group tb) gets word q = channels of its block
         // (2-bit: 4 channels 4q..4q+3, a byte each; 4-bit: channels 2q, 2q+1, two bytes each)
         constexpr int NW = BITS == 2 ? 4 : 8;
         uint32_t w[NW];
         if constexpr (BITS == 2) {
-            const uint32_t A = __builtin_amdgcn_perm(p.g[1], p.g[0], 0x05010400u);
-            const uint32_t B = __builtin_amdgcn_perm(p.g[1], p.g[0], 0x07030602u);
-            const uint32_t C = __builtin_amdgcn_perm(p.g[3], p.g[2], 0x05010400u);
-            const uint32_t E = __builtin_amdgcn_perm(p.g[3], p.g[2], 0x07030602u);
+            const uint32_t A = __builtin_amdgcn_perm(g[1], g[0], 0x05010400u);
+            const uint32_t B = __builtin_amdgcn_perm(g[1], g[0], 0x07030602u);
+            const uint32_t C = __builtin_amdgcn_perm(g[3], g[2], 0x05010400u);
+            const uint32_t E = __builtin_amdgcn_perm(g[3], g[2], 0x07030602u);
             *reinterpret_cast<uint4*>(xch + 4 * ln) =
                 make_uint4(__builtin_amdgcn_perm(C, A, 0x05040100u), __builtin_amdgcn_perm(C, A, 0x07060302u),
                            __builtin_amdgcn_perm(E, B, 0x05040100u), __builtin_amdgcn_perm(E, B, 0x07060302u));
@@ -175,8 +232,8 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
 #pragma unroll
             for (int q = 0; q < 4; ++q) w[q] = xch[4 * (base + q * R) + j];
         } else {
-            *reinterpret_cast<uint4*>(xch + 8 * ln) = make_uint4(p.g[0], p.g[1], p.g[2], p.g[3]);
-            *reinterpret_cast<uint4*>(xch + 8 * ln + 4) = make_uint4(p.g[4], p.g[5], p.g[6], p.g[7]);
+            *reinterpret_cast<uint4*>(xch + 8 * ln) = make_uint4(g[0], g[1], g[2], g[3]);
+            *reinterpret_cast<uint4*>(xch + 8 * ln + 4) = make_uint4(g[4], g[5], g[6], g[7]);
             wave_sync();
             const int j = tb & 1;
             const int base = ln - j * R;
@@ -271,7 +328,7 @@ template <int D, int BITS, bool IS_K, bool FULL>
 __device__ __forceinline__ void dequantize_run(const uint8_t* __restrict__ codes,
                                                const uint16_t* __restrict__ meta,
                                                uint16_t* __restrict__ out, int64_t n, int64_t first,
-                                               int64_t stride, int d0, uint32_t* xch) {
+                                               int64_t stride, int d0, uint32_t* xch, uint32_t* vblk) {
     constexpr int R = D / CPL;
     constexpr int64_t CB = TILE * D * BITS / 8;                     // code bytes per tile
     constexpr int64_t MH = IS_K ? 2 * D + TILE : 2 * TILE + D;      // meta halves per tile
@@ -288,10 +345,11 @@ __device__ __forceinline__ void dequantize_run(const uint8_t* __restrict__ codes
     // with no loads pending into the current registers, and the only wait
     // per tile is for the prefetched loads, issued before its stores.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    for (;;) {
+    for (int i = 0;; ++i) {
         const int64_t tn = (t + stride < n) ? t + stride : t;
         load_tile<D, BITS, IS_K>(nxt, codes + tn * CB, meta + tn * MH, tb, nb);
-        dequantize_tile<D, BITS, IS_K, FULL>(cur, d0, out + t * TILE * d0, xch + (threadIdx.x >> 6) * kWaveWords);
+        dequantize_tile<D, BITS, IS_K, FULL>(cur, d0, out + t * TILE * d0, xch + (threadIdx.x >> 6) * kWaveWords,
+                                             vblk + (i & 1) * VBlock<D, BITS>::WORDS);
         t += stride;
         if (t >= n) break;
         cur = nxt;
@@ -301,12 +359,13 @@ __device__ __forceinline__ void dequantize_run(const uint8_t* __restrict__ codes
 template <int D, int KB, int VB, bool FULL>
 __global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs args, int64_t gk) {
     __shared__ __align__(16) uint32_t xch[(2 * D / 64) * kWaveWords];
+    __shared__ __align__(16) uint32_t vblk[2 * VBlock<D, VB>::WORDS];   // V code blocks, two tiles
     const int64_t b = blockIdx.x;
     if (b < gk) {
-        dequantize_run<D, KB, true, FULL>(args.kc, args.km, args.ko, args.n_k, b, gk, args.d0, xch);
+        dequantize_run<D, KB, true, FULL>(args.kc, args.km, args.ko, args.n_k, b, gk, args.d0, xch, vblk);
     } else {
         dequantize_run<D, VB, false, FULL>(args.vc, args.vm, args.vo, args.n_v, b - gk,
-                                     (int64_t)gridDim.x - gk, args.d0, xch);
+                                     (int64_t)gridDim.x - gk, args.d0, xch, vblk);
     }
 }
 
