@@ -276,17 +276,25 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
     // The wave's 256/R tokens are one contiguous run of the output (d0
     // channels per row, 8 KB when d0 == D).  Stage it in the wave's LDS
     // region as 16-byte chunks and store it with fully contiguous 1 KB wave
-    // stores.  With an even chunk count per row the chunk index is flipped in
-    // its lowest bit by token-group parity and by the upper half of a 512-byte
-    // row, so the staging writes of a quarter wave fall on distinct banks at
-    // d0 == D.  Padded widths stage only their first d0 channels.  The store
+    // stores.  16-byte LDS stores are served eight lanes at a time over 32
+    // banks, and the eight lanes of a token group hold chunks 2 ob + h, which
+    // fill only four of the eight 16-byte bank groups.  So with 16 or 32
+    // chunks per row the chunk index is flipped in its lowest bit by bits 3
+    // and 4 of the chunk, and in bit 3 by token-group parity: eight lanes then
+    // hit eight distinct bank groups, and the quarter-wave 16-byte reads of 16
+    // consecutive chunks stay conflict-free.  With another even count (head_dim
+    // 64, or a padded width) bit 0 is flipped by token-group parity.  Padded
+    // widths stage only their first d0 channels.  The store
     // count is fixed, so the wait for the next tile's loads need not cover
     // these stores.
     {
         const int CPR = FULL ? D / 8 : d0 / 8;   // 16-byte chunks per output row
         const bool swz = FULL || (CPR & 1) == 0;
         auto slot = [&](int r, int ch) {
-            return r * CPR + (swz ? (ch ^ (((r >> 2) ^ (ch >> 4)) & 1)) : ch);
+            if (!swz) return r * CPR + ch;
+            if (CPR % 16 == 0)
+                return r * CPR + (ch ^ (((ch >> 3) ^ (ch >> 4)) & 1) ^ (((r >> 2) & 1) << 3));
+            return r * CPR + (ch ^ ((r >> 2) & 1));
         };
         const int ln = tid & 63;
         wave_sync();
