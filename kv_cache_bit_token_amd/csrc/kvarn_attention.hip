@@ -204,9 +204,20 @@ __device__ __forceinline__ float limb_join(v4i_t c) {
 
 // Per-wave LDS layout (bytes), for GQA group size G (RB = ceil(G / 4) row
 // blocks of 4 heads): the tile's meta (K then V, adjacent), the q' digit
-// image [rb][kc][lane][16 B] and the p' digit image [rb][m][lane][16 B]
+// image [rb][kc][slot][16 B] and the p' digit image [rb][m][slot][16 B]
 // (both in the matrix-core operand layout, one 16-byte read per lane), and
 // two per-head scalars of the scores (zero-point term, 1 / scale).
+//
+// Lane l reads slot l ^ s of an image, s = qa_swz(l / 16, kc) for q' and
+// l / 16 for p'.  Each slot is stored as four dwords by four lanes; without
+// the XOR, a half-wave's stores of one digit fill only 4 (q') or 8 (p') of
+// the 32 banks that 4-byte stores are served by.  The XOR moves the slots
+// of the storing lanes' different runs (q': run (gq, kc); p': lane group
+// col / 4) onto different banks, and stays inside each 16-slot group, so a
+// quarter wave still reads 16 distinct slots.
+template <int D>
+__host__ __device__ constexpr int qa_swz(int gq, int kc) { return (gq * (D / 64) + kc) & 7; }
+
 template <int D>
 struct AttnLds {
     static constexpr int KMH = 2 * D + TILE, VMH = 2 * TILE + D;
@@ -489,10 +500,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) xd[e] = fx_digits(qv[e], sq);
             digit_dwords(xd, d);
-            // rows 4 (n % 4) + digit of run (gq, kc) in row block n / 4
-            uint8_t* dst = qaimg + (((n >> 2) * NKC + kc) * 4 + gq) * 256 + 4 * (n & 3) * 16 + 4 * j;
+            // rows 4 (n % 4) + digit of run (gq, kc) in row block n / 4: slot
+            // 16 gq + 4 (n % 4) + digit of image (n / 4, kc), swizzled
+            const int sl = (16 * gq + 4 * (n & 3)) ^ qa_swz<D>(gq, kc);
+            uint8_t* dst = qaimg + ((n >> 2) * NKC + kc) * 1024 + 4 * j;
 #pragma unroll
-            for (int dg = 0; dg < 4; ++dg) *reinterpret_cast<uint32_t*>(dst + 16 * dg) = d[dg];
+            for (int dg = 0; dg < 4; ++dg) *reinterpret_cast<uint32_t*>(dst + 16 * (sl ^ dg)) = d[dg];
             if (rem == 0) {
                 st_qz[n] = zt;
                 st_iq[n] = 1.0f / (sq * (float)(256 >> KB));   // the codes enter as 2^(8-KB) (c - MK)
@@ -509,7 +522,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 if (rb < RB) {
 #pragma unroll
                     for (int kc = 0; kc < NKC; ++kc)
-                        qa[rb][kc] = *reinterpret_cast<const v4i_t*>(qaimg + (rb * NKC + kc) * 1024 + 16 * lane);
+                        qa[rb][kc] = *reinterpret_cast<const v4i_t*>(
+                            qaimg + (rb * NKC + kc) * 1024 + 16 * (lane ^ qa_swz<D>(lane >> 4, kc)));
                 }
             }
             float qz[RBMAX], iq[RBMAX];
@@ -580,9 +594,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) xd[e] = fx_digits(p[4 * m + e], sp);
                         digit_dwords(xd, d);
-                        uint8_t* dst = paimg + ((rb * 2 + m) * 4 + (col >> 2)) * 256 + 4 * lgr * 16 + 4 * (col & 3);
+                        // slot 16 (col / 4) + 4 lgr + digit, swizzled by col / 4
+                        uint8_t* dst = paimg + (rb * 2 + m) * 1024 + 16 * (16 * (col >> 2) + 4 * lgr) + 4 * (col & 3);
 #pragma unroll
-                        for (int dg = 0; dg < 4; ++dg) *reinterpret_cast<uint32_t*>(dst + 16 * dg) = d[dg];
+                        for (int dg = 0; dg < 4; ++dg)
+                            *reinterpret_cast<uint32_t*>(dst + 16 * (dg ^ (col >> 2))) = d[dg];
                     }
                 }
             }
@@ -597,7 +613,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 if (rb < RB) {
 #pragma unroll
                     for (int m = 0; m < 2; ++m)
-                        pa[rb][m] = *reinterpret_cast<const v4i_t*>(paimg + (rb * 2 + m) * 1024 + 16 * lane);
+                        pa[rb][m] = *reinterpret_cast<const v4i_t*>(paimg + (rb * 2 + m) * 1024 + 16 * (lane ^ (lane >> 4)));
                 }
             }
 #pragma unroll
