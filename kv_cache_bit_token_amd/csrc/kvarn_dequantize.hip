@@ -10,10 +10,11 @@
 // fp16 (nearest even).
 //
 // 2*D threads per workgroup, same register layout and transform network as
-// the quantiser (kvarn_device.hpp).  A workgroup walks a strided sequence of
-// tiles (K tiles or V tiles) and loads the packed codes and meta of the next
-// tile into registers while it transforms the current one, so the HBM
-// latency of the (small) packed input overlaps the arithmetic.  K codes are
+// the quantiser (kvarn_device.hpp).  One workgroup per tile, K tiles then V
+// tiles, launched in address order: the device writes fastest when the
+// workgroups in flight write one narrow, advancing window of addresses, and
+// the resident workgroups (three per CU) overlap one another's HBM
+// latency with their arithmetic and stores.  K codes are
 // token-major, so a lane's 16 channels of one token are one 8- (4-bit) or
 // 4-byte (2-bit) word, read by that lane alone.  V codes are channel-major:
 // a wavefront's tokens are a few bytes of every channel row, so the
@@ -158,7 +159,6 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
     const float rsqrtD = 1.0f / __builtin_sqrtf((float)D);
     uint32_t* mw = xch + kMetaWord;        // the wave's meta words (2 halves each)
 
-    wave_sync();   // the previous tile's reads of this wave's LDS are done
 #pragma unroll
     for (int k = 0; k < MP::NS; ++k)
         if (ln + 64 * k < MP::NC) *reinterpret_cast<uint4*>(mw + 4 * (ln + 64 * k)) = p.m[k];
@@ -189,9 +189,8 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
         // (channel row r, words w0 .. w0 + 3), then lane (tb, nb) reads word
         // m of the rows it swaps below, g[n] = row 16 nb + 4 j + n (2-bit,
         // m = tb / 4, j = tb % 4) or g[q] = row 16 nb + 2 q + j (4-bit,
-        // m = tb / 2, j = tb % 2).  vb alternates between two buffers from
-        // tile to tile, so one barrier per tile orders the stores after the
-        // reads of two tiles back.
+        // m = tb / 2, j = tb % 2).  The workgroup dequantises one tile, so
+        // the block is stored once and one barrier orders the reads after it.
         using VBk = VBlock<D, BITS>;
         uint32_t g[BITS == 2 ? 4 : 8];
 #pragma unroll
@@ -284,9 +283,7 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
     // hit eight distinct bank groups, and the quarter-wave 16-byte reads of 16
     // consecutive chunks stay conflict-free.  With another even count (head_dim
     // 64, or a padded width) bit 0 is flipped by token-group parity.  Padded
-    // widths stage only their first d0 channels.  The store
-    // count is fixed, so the wait for the next tile's loads need not cover
-    // these stores.
+    // widths stage only their first d0 channels.
     {
         const int CPR = FULL ? D / 8 : d0 / 8;   // 16-byte chunks per output row
         const bool swz = FULL || (CPR & 1) == 0;
@@ -330,81 +327,46 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
     }
 }
 
-// Tiles first, first + stride, ... of one tensor, the next tile's packed
-// input in flight while the current one is transformed.
-template <int D, int BITS, bool IS_K, bool FULL>
-__device__ __forceinline__ void dequantize_run(const uint8_t* __restrict__ codes,
-                                               const uint16_t* __restrict__ meta,
-                                               uint16_t* __restrict__ out, int64_t n, int64_t first,
-                                               int64_t stride, int d0, uint32_t* xch, uint32_t* vblk) {
-    constexpr int R = D / CPL;
-    constexpr int64_t CB = TILE * D * BITS / 8;                     // code bytes per tile
-    constexpr int64_t MH = IS_K ? 2 * D + TILE : 2 * TILE + D;      // meta halves per tile
-    const int tid = threadIdx.x;
-    const int cb = tid % R;
-    const int tb = tid / R;
-    const int nb = cb ^ Net<R>::kF;   // rotated channel block read by this lane
-    // The prefetch is unconditional (the last one re-reads the current
-    // tile) so that the wait before each tile covers exactly one tile's loads.
-    Packed<D, BITS, IS_K> cur, nxt;
-    int64_t t = first;
-    load_tile<D, BITS, IS_K>(cur, codes + t * CB, meta + t * MH, tb, nb);
-    // Wait for the first tile here, once: the loop then starts every tile
-    // with no loads pending into the current registers, and the only wait
-    // per tile is for the prefetched loads, issued before its stores.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    for (int i = 0;; ++i) {
-        const int64_t tn = (t + stride < n) ? t + stride : t;
-        load_tile<D, BITS, IS_K>(nxt, codes + tn * CB, meta + tn * MH, tb, nb);
-        dequantize_tile<D, BITS, IS_K, FULL>(cur, d0, out + t * TILE * d0, xch + (threadIdx.x >> 6) * kWaveWords,
-                                             vblk + (i & 1) * VBlock<D, BITS>::WORDS);
-        t += stride;
-        if (t >= n) break;
-        cur = nxt;
-    }
-}
+// Workgroup b dequantises tile b0 + b of the concatenation [K tiles | V
+// tiles].  The grid covers every tile (in launches of at most kMaxGrid
+// workgroups), so the workgroups in flight write one narrow window of the
+// outputs that advances in address order, the pattern the device writes
+// fastest; the resident workgroups overlap one another's loads and stores.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 
 template <int D, int KB, int VB, bool FULL>
-__global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs args, int64_t gk) {
+__global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs a, int64_t b0) {
     __shared__ __align__(16) uint32_t xch[(2 * D / 64) * kWaveWords];
-    __shared__ __align__(16) uint32_t vblk[2 * VBlock<D, VB>::WORDS];   // V code blocks, two tiles
-    const int64_t b = blockIdx.x;
-    if (b < gk) {
-        dequantize_run<D, KB, true, FULL>(args.kc, args.km, args.ko, args.n_k, b, gk, args.d0, xch, vblk);
-    } else {
-        dequantize_run<D, VB, false, FULL>(args.vc, args.vm, args.vo, args.n_v, b - gk,
-                                     (int64_t)gridDim.x - gk, args.d0, xch, vblk);
+    __shared__ __align__(16) uint32_t vblk[VBlock<D, VB>::WORDS];   // the V tile's code block
+    constexpr int R = D / CPL;
+    const int tid = threadIdx.x;
+    const int tb = tid / R;
+    const int nb = (tid % R) ^ Net<R>::kF;   // rotated channel block read by this lane
+    uint32_t* xw = xch + (tid >> 6) * kWaveWords;
+    const int64_t b = b0 + blockIdx.x;
+    if (b < a.n_k) {
+        Packed<D, KB, true> p;
+        load_tile<D, KB, true>(p, a.kc + b * (TILE * D * KB / 8), a.km + b * (2 * D + TILE), tb, nb);
+        dequantize_tile<D, KB, true, FULL>(p, a.d0, a.ko + b * TILE * a.d0, xw, vblk);
+    } else if (b < a.n_k + a.n_v) {
+        const int64_t t = b - a.n_k;
+        Packed<D, VB, false> p;
+        load_tile<D, VB, false>(p, a.vc + t * (TILE * D * VB / 8), a.vm + t * (2 * TILE + D), tb, nb);
+        dequantize_tile<D, VB, false, FULL>(p, a.d0, a.vo + t * TILE * a.d0, xw, vblk);
     }
 }
 
-// Grid: as many workgroups as fit on the device at once (at most one per
-// tile), split between K and V in proportion to their tile counts.
 template <int D, int KB, int VB>
 static hipError_t launch_dq(const DequantArgs& a, hipStream_t s) {
     auto kern = (a.d0 == D) ? dequantize_kernel<D, KB, VB, true> : dequantize_kernel<D, KB, VB, false>;
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 2 * D, 0);
-    if (e != hipSuccess) return e;
     const int64_t total = a.n_k + a.n_v;
-    const int64_t parts = (a.n_k > 0) + (a.n_v > 0);
-    int64_t g = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-    if (g > total) g = total;
-    if (g < parts) g = parts;
-    int64_t gk = 0, gv = 0;
-    if (a.n_k > 0) {
-        gk = (g * a.n_k + total / 2) / total;
-        if (gk < 1) gk = 1;
-        if (a.n_v > 0 && gk > g - 1) gk = g - 1;
-        if (gk > a.n_k) gk = a.n_k;
+    for (int64_t b0 = 0; b0 < total; b0 += kMaxGrid) {
+        const int64_t n = total - b0 < kMaxGrid ? total - b0 : kMaxGrid;
+        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(2 * D), 0, s, a, b0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (a.n_v > 0) {
-        gv = g - gk;
-        if (gv > a.n_v) gv = a.n_v;
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(gk + gv)), dim3(2 * D), 0, s, a, gk);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <int D>
