@@ -77,38 +77,38 @@ def quant_ops_per_elem(D, n_iters):
 TRAFFIC = {
     ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295724054,
                               "write_bytes": 906053472},
-    ("dequantize", "prefill"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 924491478,
-                                "write_bytes": 4294990976},
-    ("decode_attention", "prefill"): {"source_sha256": "591a44c69555628e", "fetch_bytes": 922682888,
-                                      "write_bytes": 14953056},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 2454535953,
-                                              "write_bytes": 8590094348},
+    ("dequantize", "prefill"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 906511044,
+                                "write_bytes": 4294978688},
+    ("decode_attention", "prefill"): {"source_sha256": "60c83e300b90b04b", "fetch_bytes": 922677343,
+                                      "write_bytes": 14950880},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 1812082852,
+                                              "write_bytes": 8590330240},
     ("quantize", "head_dim_64_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67465886,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 15141639,
-                                            "write_bytes": 67123744},
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 15129146,
+                                            "write_bytes": 67114752},
     ("quantize", "head_dim_64_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67464930,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 15141468,
-                                            "write_bytes": 67135691},
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 15129146,
+                                            "write_bytes": 67119936},
     ("quantize", "head_dim_96_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101036578,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 28567101,
-                                            "write_bytes": 100677173},
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 28594342,
+                                            "write_bytes": 100663296},
     ("quantize", "head_dim_96_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101035183,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 28566760,
-                                            "write_bytes": 100678912},
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 28594342,
+                                            "write_bytes": 100663296},
     ("quantize", "head_dim_256_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268844605,
                                            "write_bytes": 55050861},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 57841212,
-                                             "write_bytes": 268481685},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 55275910,
+                                             "write_bytes": 268475648},
     ("quantize", "head_dim_256_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268842762,
                                            "write_bytes": 55051102},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "a41aeffb0b7c7106", "fetch_bytes": 57739412,
-                                             "write_bytes": 268505696},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "591a44c69555628e", "fetch_bytes": 1828609017,
-                                                          "write_bytes": 15108329},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 55275910,
+                                             "write_bytes": 268516416},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "60c83e300b90b04b", "fetch_bytes": 1828593077,
+                                                          "write_bytes": 15124416},
     ("fp16_decode_attention", "prefill"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 4714063900,
                                            "write_bytes": 18111978},
     ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 9293708088,
@@ -321,9 +321,13 @@ def stream_reference(dev, units, reps=5):
     fraction beside the nominal 8 TB/s.  Best over kernel layouts (a loop
     kernel; an unrolled one with plain or nontemporal stores; for the
     dequantize mix also phased kernels that read 4 or 8 units before writing
-    them), each at three persistent grid sizes; `variants` keeps every
-    layout's best rate.  `fp16_write` is the dequantiser's output alone
-    (write-only, the same 4.3 GB)."""
+    them) and grid shapes: persistent grids of 4, 8 and 16 workgroups per CU,
+    and grids with one workgroup per unit in address order, the unit a tile
+    pair, a single tile (half the words) or a sixteenth of a pair (4 KB of
+    fp16).  `variants` keeps every layout's
+    best rate and `grids` the grid shape it was reached with; `by_grid_GBps`
+    the best rate of each grid shape over the layouts.  `fp16_write` is
+    the dequantiser's output alone (write-only, the same 4.3 GB)."""
     import ctypes
     import torch
 
@@ -346,12 +350,19 @@ def stream_reference(dev, units, reps=5):
     out = {}
     for name, (rq, wq, kinds) in mixes.items():
         nbytes = units * (rq + wq) * 16
-        variants = {}
+        # (label, units, rq, wq, workgroups)
+        grids = [("%d_per_cu" % k, units, rq, wq, cus * k) for k in (4, 8, 16)]
+        grids.append(("one_per_tile_pair", units, rq, wq, units))
+        grids.append(("one_per_tile", 2 * units, rq // 2, wq // 2, 2 * units))
+        grids.append(("one_per_16th_pair", 16 * units, rq // 16, wq // 16, 16 * units))
+        variants, shapes, by_grid = {}, {}, {}
         for unrolled in kinds:
             best = None
-            for per_cu in (4, 8, 16):
+            for label, n, r, w, blocks in grids:
+                if unrolled >= 3 and (r, w) != (rq, wq):
+                    continue   # the phased kernels exist for the tile-pair unit only
                 def run():
-                    st = fn(src.data_ptr(), dst.data_ptr(), units, rq, wq, cus * per_cu, unrolled,
+                    st = fn(src.data_ptr(), dst.data_ptr(), n, r, w, blocks, unrolled,
                             sink.data_ptr(), stream)
                     if st != 0:
                         raise RuntimeError("stream reference launch failed: %d" % st)
@@ -365,13 +376,18 @@ def stream_reference(dev, units, reps=5):
                 e1.record()
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / reps
-                best = ms if best is None else min(best, ms)
-            variants[layouts[unrolled]] = round(nbytes / (best / 1e3) / 1e9, 1)
+                rate = round(nbytes / (ms / 1e3) / 1e9, 1)
+                by_grid[label] = max(by_grid.get(label, 0.0), rate)
+                if best is None or ms < best[0]:
+                    best = (ms, label)
+            variants[layouts[unrolled]] = round(nbytes / (best[0] / 1e3) / 1e9, 1)
+            shapes[layouts[unrolled]] = best[1]
         top = max(variants, key=variants.get)
         gbs = variants[top]
         out[name] = {"ms": round(nbytes / (gbs * 1e9) * 1e3, 4), "GBps": gbs,
                      "frac_of_peak": round(gbs * 1e9 / HBM_PEAK, 4), "best_layout": top,
-                     "variants_GBps": variants}
+                     "best_grid": shapes[top], "variants_GBps": variants, "grids": shapes,
+                     "by_grid_GBps": by_grid}
     del src, dst
     torch.cuda.empty_cache()
     return out

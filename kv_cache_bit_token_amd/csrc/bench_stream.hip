@@ -229,10 +229,12 @@ extern "C" int kvarn_valu_class_reference(int32_t cls, void* out, int32_t blocks
     return (int)hipGetLastError();
 }
 
-// Streams `units` units through a persistent grid of `blocks` workgroups of
-// 256 threads; with `unrolled` 1 (2: nontemporal stores), the tile-pair
-// mixes at head_dim 128 use the compile-time kernels (others fall back to the
-// loop kernel); `unrolled` 3 / 4 run the dequantize mix phased, 4 / 8 units
+// Streams `units` units through a grid of `blocks` workgroups of 256 threads
+// (each takes units blockIdx, blockIdx + blocks, ...: a persistent grid when
+// blocks < units, one unit per workgroup in address order when blocks ==
+// units); with `unrolled` 1 (2: nontemporal stores), the tile-pair and
+// single-tile mixes at head_dim 128 use the compile-time kernels (others fall
+// back to the loop kernel); `unrolled` 3 / 4 run the dequantize mix phased, 4 / 8 units
 // read before their writes.  src holds units * rq words, dst units * wq words, sink 256
 // words; device pointers, 16-byte aligned.  Returns the hipError_t of the
 // launch (0 on success).
@@ -271,6 +273,11 @@ extern "C" int kvarn_stream_reference(const void* src, void* dst, int64_t units,
     KVARN_FIXED(864, 0)
     KVARN_FIXED(4096, 0)
     KVARN_FIXED(0, 4096)
+    KVARN_FIXED(2048, 432)
+    KVARN_FIXED(432, 2048)
+    KVARN_FIXED(432, 0)
+    KVARN_FIXED(2048, 0)
+    KVARN_FIXED(0, 2048)
 #undef KVARN_FIXED
     hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
