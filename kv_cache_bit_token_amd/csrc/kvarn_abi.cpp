@@ -183,8 +183,7 @@ kvarn_status kvarn_decode_attention_workspace(const kvarn_params* params, int32_
     if (st != KVARN_OK) return st;
     st = check_attention_shape(batch, n_q_heads, n_kv_heads, tiles_per_seq);
     if (st != KVARN_OK) return st;
-    int ns = 0, tps = 0;
-    kvarn::attention_plan(batch, n_kv_heads, tiles_per_seq, &ns, &tps);
+    const int ns = kvarn::attention_splits(batch, n_kv_heads, tiles_per_seq);
     *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
     return KVARN_OK;
 }
@@ -212,8 +211,7 @@ kvarn_status decode_attention_impl(const kvarn_params* params, int32_t batch, in
     if (misaligned(q_fp16) || misaligned(out) || misaligned(k_codes) || misaligned(v_codes) ||
         misaligned(k_meta) || misaligned(v_meta) || misaligned(workspace))
         return KVARN_E_ALIGN;
-    int ns = 0, tps = 0;
-    kvarn::attention_plan(batch, n_kv_heads, tiles_per_seq, &ns, &tps);
+    const int ns = kvarn::attention_splits(batch, n_kv_heads, tiles_per_seq);
     const size_t need = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
     if (use_static) workspace_bytes = kvarn::kStaticScratchBytes;
     if (tiles_per_seq > 0 && workspace_bytes < need) return KVARN_E_WORKSPACE;
@@ -236,7 +234,6 @@ kvarn_status decode_attention_impl(const kvarn_params* params, int32_t batch, in
     a.n_kv_heads = n_kv_heads;
     a.tiles_per_seq = tiles_per_seq;
     a.n_splits = ns;
-    a.tiles_per_split = tps;
     a.n_parts = ns;
     a.d0 = params->head_dim;
     a.sm_scale = sm_scale;
@@ -315,8 +312,7 @@ kvarn_status kvarn_decode_attention_paged_workspace(const kvarn_params* params, 
     if (st != KVARN_OK) return st;
     st = check_attention_shape(batch, n_q_heads, n_kv_heads, max_blocks);
     if (st != KVARN_OK) return st;
-    int ns = 0, tps = 0;
-    kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
+    int ns = kvarn::attention_splits(batch, n_kv_heads, max_blocks);
     if (max_blocks == 0) ns = 0;
     *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
     return KVARN_OK;
@@ -348,8 +344,7 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t ba
         misaligned(block_table) || misaligned(k_codes) || misaligned(v_codes) ||
         misaligned(k_meta) || misaligned(v_meta))
         return KVARN_E_ALIGN;
-    int ns = 0, tps = 0;
-    kvarn::attention_plan(batch, n_kv_heads, max_blocks, &ns, &tps);
+    int ns = kvarn::attention_splits(batch, n_kv_heads, max_blocks);
     if (max_blocks == 0) ns = 0;
     if (workspace_bytes < kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
         return KVARN_E_WORKSPACE;
@@ -369,7 +364,6 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t ba
     a.tiles_per_seq = max_blocks;
     // without a pool no packed tile is read: only the tail's partial slot
     a.n_splits = packed ? ns : 0;
-    a.tiles_per_split = tps;
     a.n_parts = (packed ? ns : 0) + 1;
     a.d0 = params->head_dim;
     a.sm_scale = sm_scale;

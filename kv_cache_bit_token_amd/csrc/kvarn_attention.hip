@@ -45,9 +45,12 @@
 // writes whole dwords of the p' image; the only LDS round trips per tile
 // are the meta, the q' image and the p' image.
 //
-// Work split: each wavefront owns one split (a run of tiles) of one
-// (b, KV head) and every query head of that head's GQA group; these waves
-// never synchronise with each other.  A paged call's fp16 tails run as
+// Work split: each wavefront owns one split of one (b, KV head) and every
+// query head of that head's GQA group; these waves never synchronise with
+// each other.  Split s of n takes tiles s, s + n, s + 2n, ... of the
+// sequence, so the n waves of a sequence read n neighbouring tiles at a time
+// and the device reads a few hundred short windows instead of one long run
+// per wave.  A paged call's fp16 tails run as
 // extra 256-thread workgroups of the same grid where its workgroups have
 // 256 threads (they synchronise only among their own waves), else as a
 // kernel of their own.  A combine kernel merges the splits' (max, sum, acc)
@@ -60,23 +63,23 @@ namespace kvarn {
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTargetWaves = 6144;   // splits: two rounds of 3 resident waves on each of the 1024 SIMDs
+// Splits in total: about four per SIMD.  With strided splits this measured
+// fastest on the 64 x 8 x 16384 and 64 x 8 x 32768 caches (eight splits per
+// sequence, which divide their 128 and 256 tiles evenly); 7, 9, 10 or 12
+// splits per sequence were 3-10 % slower.
+constexpr int kTargetWaves = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 
-void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
-                    int* tiles_per_split) {
+// Splits per (b, KV head): about kTargetWaves in total, at most one per tile,
+// and no more than the tile count needs at that many tiles per split.
+int attention_splits(int batch, int n_kv_heads, int tiles_per_seq) {
     const int64_t pairs = (int64_t)batch * n_kv_heads;
-    int ns = 1;
-    if (pairs > 0 && tiles_per_seq > 0) {
-        int64_t want = (kTargetWaves + pairs - 1) / pairs;
-        if (want > tiles_per_seq) want = tiles_per_seq;
-        if (want < 1) want = 1;
-        ns = (int)want;
-    }
-    int tps = tiles_per_seq > 0 ? (tiles_per_seq + ns - 1) / ns : 0;
-    if (tps > 0) ns = (tiles_per_seq + tps - 1) / tps;
-    *n_splits = ns;
-    *tiles_per_split = tps;
+    if (pairs <= 0 || tiles_per_seq <= 0) return 1;
+    int64_t want = (kTargetWaves + pairs - 1) / pairs;
+    if (want > tiles_per_seq) want = tiles_per_seq;
+    if (want < 1) want = 1;
+    const int64_t per = (tiles_per_seq + want - 1) / want;
+    return (int)((tiles_per_seq + per - 1) / per);
 }
 
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
@@ -327,8 +330,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     // tiles of this (b, g): all tiles_per_seq, or the sequence's used blocks
     int ntiles = a.tiles_per_seq;
     if (a.table) ntiles = min(max(a.nblk[b], 0), a.tiles_per_seq);
-    const int t0 = split * a.tiles_per_split;
-    const int t1 = min(t0 + a.tiles_per_split, ntiles);
+    // strided splits: step k of split s reads tile s + k * n_splits
+    const int t0 = 0;
+    const int t1 = split < ntiles ? (ntiles - split + a.n_splits - 1) / a.n_splits : 0;
     if (t0 >= t1) {
         // nothing in this split: an empty partial (m = -inf, l = 0, acc = 0)
         for (int k = lane; k < G * (D + 2); k += 64) {
@@ -365,14 +369,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     // lane, so a tile's id is a lane read instead of a scalar load on the
     // prefetch path
     int blk_lane = 0;
-    if (a.table && t0 + lane < t1) blk_lane = a.table[(size_t)b * a.tiles_per_seq + t0 + lane];
+    if (a.table && t0 + lane < t1) blk_lane = a.table[(size_t)b * a.tiles_per_seq + split + (t0 + lane) * a.n_splits];
     // pool index of tile ti of this (b, g) (past the split's end: its last
     // tile; a paged table entry outside the pool reads block 0)
     auto tile_index = [&](int ti) -> int64_t {
         const int tc = ti < t1 ? ti : t1 - 1;
-        if (!a.table) return (int64_t)bg * a.tiles_per_seq + tc;
+        const int lt = split + tc * a.n_splits;
+        if (!a.table) return (int64_t)bg * a.tiles_per_seq + lt;
         int64_t blk = (tc - t0 < 64) ? __builtin_amdgcn_readlane(blk_lane, tc - t0)
-                                     : a.table[(size_t)b * a.tiles_per_seq + tc];
+                                     : a.table[(size_t)b * a.tiles_per_seq + lt];
         if (blk < 0 || blk >= a.pool_blocks) blk = 0;
         return blk * a.n_kv_heads + g;
     };

@@ -48,8 +48,7 @@ struct AttnArgs {
     int n_q_heads;
     int n_kv_heads;
     int tiles_per_seq;
-    int n_splits;        // splits per (b, g) of the packed tiles
-    int tiles_per_split;
+    int n_splits;        // splits per (b, g) of the packed tiles; split s takes tiles s, s + n_splits, ...
     int d0;
     float sm_scale;
     int n_parts = 0;     // partial slots per (b, h) in the workspace (n_splits, + 1 with a tail)
@@ -92,8 +91,7 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_
 
 // Split-K plan of the decode attention for a shape (shared by the workspace
 // query and the launch, so both agree).
-void attention_plan(int batch, int n_kv_heads, int tiles_per_seq, int* n_splits,
-                    int* tiles_per_split);
+int attention_splits(int batch, int n_kv_heads, int tiles_per_seq);
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 // Packed-cache attention: the split partials, then the rotated queries.
 size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
