@@ -79,8 +79,8 @@ TRAFFIC = {
                               "write_bytes": 906053472},
     ("dequantize", "prefill"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 906511044,
                                 "write_bytes": 4294978688},
-    ("decode_attention", "prefill"): {"source_sha256": "60c83e300b90b04b", "fetch_bytes": 922677343,
-                                      "write_bytes": 14950880},
+    ("decode_attention", "prefill"): {"source_sha256": "d323bd7d48b05bde", "fetch_bytes": 917367422,
+                                      "write_bytes": 10617824},
     ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 1812082852,
                                               "write_bytes": 8590330240},
     ("quantize", "head_dim_64_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67465886,
@@ -107,8 +107,8 @@ TRAFFIC = {
                                            "write_bytes": 55051102},
     ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 55275910,
                                              "write_bytes": 268516416},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "60c83e300b90b04b", "fetch_bytes": 1828593077,
-                                                          "write_bytes": 15124416},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "d323bd7d48b05bde", "fetch_bytes": 1823290068,
+                                                          "write_bytes": 10643744},
     ("fp16_decode_attention", "prefill"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 4714063900,
                                            "write_bytes": 18111978},
     ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 9293708088,

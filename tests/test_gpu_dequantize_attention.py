@@ -124,12 +124,13 @@ def test_attention_empty_cache_is_zero():
     assert not out.cpu().numpy().any()
 
 
-@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(512, 8, 32, 13, 128), (1024, 4, 32, 9, 64)])
+@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(256, 8, 32, 13, 128), (512, 4, 32, 9, 64)])
 def test_attention_several_tiles_per_split(B, n_kv, Hq, tps, d0):
     """Enough (sequence, KV head) pairs that each split runs several tiles
-    (4096 pairs -> 2 splits per pair: 7 + 6 and 5 + 4 tiles), so the online
-    softmax rescales across a split's tiles and the next-tile prefetch runs
-    inside a split.  The cache is assembled from 256 oracle-quantised tiles of
+    (2048 pairs -> 2 splits per pair, split s taking every other tile from
+    tile s: 7 + 6 and 5 + 4 tiles), so the online softmax rescales across a
+    split's tiles, the next-tile prefetch runs inside a split, and the combine
+    merges interleaved splits.  The cache is assembled from 256 oracle-quantised tiles of
     the config-1 recipe, drawn at random per position; the host checks that a
     later tile of a split often holds a head's largest score, so the running
     maximum really moves inside splits."""
@@ -149,14 +150,15 @@ def test_attention_several_tiles_per_split(B, n_kv, Hq, tps, d0):
     record("attention, several tiles per split %s" % ((B, n_kv, Hq, tps, d0),),
            compare_attention(out.cpu().numpy(), ref,
                              packed_cache(q, kc, vc, km, vm, n_kv, tps)))
-    # the first split of each of the first 8 sequences' (KV head, query head):
-    # in how many does the largest score sit past the split's first tile?
+    # the first split (tiles 0, 2, 4, ...) of each of the first 8 sequences'
+    # (KV head, query head): in how many does the largest score sit past the
+    # split's first tile?
     kd, _ = oracle.dequantize_tiles(qk["codes"], qk["meta"], d0, 4, True)    # [256][128][d0]
-    G, first = Hq // n_kv, (tps + 1) // 2
+    G = Hq // n_kv
     later = total = 0
     for b in range(8):
         for g in range(n_kv):
-            tiles = idx[(b * n_kv + g) * tps:(b * n_kv + g) * tps + first]
+            tiles = idx[(b * n_kv + g) * tps + np.arange(0, tps, 2)]
             keys = kd[tiles].reshape(-1, d0)
             s = q[b, g * G:(g + 1) * G].astype(np.float64) @ keys.T
             later += int((s.argmax(axis=1) >= 128).sum())
