@@ -75,51 +75,52 @@ def quant_ops_per_elem(D, n_iters):
 # decode_attention sums the query rotation, the split partials and the
 # combine; fp16_decode_attention its partials and combine.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 4295724054,
-                              "write_bytes": 906053472},
-    ("dequantize", "prefill"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 906511044,
-                                "write_bytes": 4294978688},
-    ("decode_attention", "prefill"): {"source_sha256": "d323bd7d48b05bde", "fetch_bytes": 917367422,
-                                      "write_bytes": 10617824},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 1812082852,
-                                              "write_bytes": 8590330240},
-    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67465886,
+    ("quantize", "prefill"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 4295665558,
+                              "write_bytes": 905969664},
+    ("dequantize", "prefill"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 906530883,
+                                "write_bytes": 4295021504},
+    ("decode_attention", "prefill"): {"source_sha256": "d0287558aac26105", "fetch_bytes": 917365886,
+                                      "write_bytes": 10617376},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 1812082596,
+                                              "write_bytes": 8590379008},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 67458968,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 15129146,
-                                            "write_bytes": 67114752},
-    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 67464930,
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 15129146,
+                                            "write_bytes": 67117184},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 67458840,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 15129146,
-                                            "write_bytes": 67119936},
-    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101036578,
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 15129146,
+                                            "write_bytes": 67121408},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 101040297,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 101035183,
+    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 101040297,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268844605,
-                                           "write_bytes": 55050861},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 55275910,
-                                             "write_bytes": 268475648},
-    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "cd30c71b1ec7d072", "fetch_bytes": 268842762,
-                                           "write_bytes": 55051102},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "1f68243f943707e5", "fetch_bytes": 55275910,
-                                             "write_bytes": 268516416},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "d323bd7d48b05bde", "fetch_bytes": 1823290068,
-                                                          "write_bytes": 10643744},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 4714063900,
-                                           "write_bytes": 18111978},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "101f46a3dce2282e", "fetch_bytes": 9293708088,
-                                                               "write_bytes": 18154938},
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 268855934,
+                                           "write_bytes": 55050240},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 55275910,
+                                             "write_bytes": 268496832},
+    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 268855038,
+                                           "write_bytes": 55050240},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 55275910,
+                                             "write_bytes": 268520128},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "d0287558aac26105", "fetch_bytes": 1823291092,
+                                                          "write_bytes": 10642400},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "c199b82bdd2de962", "fetch_bytes": 4712029131,
+                                           "write_bytes": 18116832},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "c199b82bdd2de962", "fetch_bytes": 9296548359,
+                                                               "write_bytes": 18144608},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {
-    "quantize": ("kvarn_quantize.hip", "kvarn_device.hpp"),
-    "dequantize": ("kvarn_dequantize.hip", "kvarn_device.hpp"),
-    "decode_attention": ("kvarn_attention.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp"),
-    "fp16_decode_attention": ("kvarn_attention_fp16.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp"),
+    "quantize": ("kvarn_quantize.hip", "kvarn_device.hpp", "kvarn_internal.hpp"),
+    "dequantize": ("kvarn_dequantize.hip", "kvarn_device.hpp", "kvarn_internal.hpp"),
+    "decode_attention": ("kvarn_attention.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp", "kvarn_internal.hpp"),
+    "fp16_decode_attention": ("kvarn_attention_fp16.hip", "kvarn_device.hpp", "kvarn_rsrc.hpp",
+                              "kvarn_internal.hpp"),
 }
 
 

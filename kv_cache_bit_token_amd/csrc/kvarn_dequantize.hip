@@ -332,7 +332,6 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
 // workgroups), so the workgroups in flight write one narrow window of the
 // outputs that advances in address order, the pattern the device writes
 // fastest; the resident workgroups overlap one another's loads and stores.
-constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 
 template <int D, int KB, int VB, bool FULL>
 __global__ __launch_bounds__(2 * D) void dequantize_kernel(DequantArgs a, int64_t b0) {

@@ -9,6 +9,12 @@
 
 namespace kvarn {
 
+// Workgroups per launch of the kernels that give each tile its own workgroup:
+// at up to 512 threads each, far inside a dispatch's 2^32 work-items.  Larger
+// tile counts are launched in chunks, each kernel taking its first tile as an
+// argument.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+
 struct QuantArgs {
     const uint16_t* k;  // [n_k][128][d0] fp16 bits
     const uint16_t* v;  // [n_v][128][d0]

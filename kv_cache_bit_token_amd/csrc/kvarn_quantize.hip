@@ -532,9 +532,9 @@ template <int D>
 constexpr int quant_lds_floats() { return 4 * (CPL + 1) * D + 2 * (D + D / 4) + 4 + 16; }
 
 template <int D, int KB, int VB, bool FULL>
-__global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
+__global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args, int64_t b0) {
     __shared__ __align__(16) float lds[quant_lds_floats<D>()];
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = b0 + blockIdx.x;   // K tiles, then V tiles
     const bool is_k = tile < args.n_k;
     const int64_t src = is_k ? tile : tile - args.n_k;
     // output slot: the tile itself, or its entry of dst (out-of-range entries
@@ -555,14 +555,18 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantArgs args) {
     }
 }
 
+// One workgroup per tile, in launches of at most kMaxGrid workgroups.
 template <int D, int KB, int VB>
 static hipError_t launch_q(const QuantArgs& a, hipStream_t s) {
-    const int64_t blocks = a.n_k + a.n_v;
-    if (a.d0 == D)
-        hipLaunchKernelGGL((quantize_kernel<D, KB, VB, true>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
-    else
-        hipLaunchKernelGGL((quantize_kernel<D, KB, VB, false>), dim3((unsigned)blocks), dim3(2 * D), 0, s, a);
-    return hipGetLastError();
+    auto kern = (a.d0 == D) ? quantize_kernel<D, KB, VB, true> : quantize_kernel<D, KB, VB, false>;
+    const int64_t total = a.n_k + a.n_v;
+    for (int64_t b0 = 0; b0 < total; b0 += kMaxGrid) {
+        const int64_t n = total - b0 < kMaxGrid ? total - b0 : kMaxGrid;
+        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(2 * D), 0, s, a, b0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D>

@@ -29,8 +29,8 @@ import torch
 import kv_cache_bit_token_amd as kv
 import oracle
 from kv_cache_bit_token_amd import synthetic
-from parity import (CodeTally, compare_attention, compare_dequant, compare_meta, fp16_cache,
-                    packed_cache, record)
+from parity import (CodeTally, compare_attention, compare_codes, compare_dequant, compare_meta,
+                    fp16_cache, packed_cache, record)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(400)]
 
@@ -229,4 +229,48 @@ def test_decode_attention_fp16_full_size():
     record("fp16 decode attention 64x32x32768",
            compare_attention(_host(out), ref, fp16_cache(qh, kh, vh)))
     del k, v
+    _free()
+
+
+def test_launch_chunks_quantize_dequantize():
+    """More tiles than one launch takes: the quantiser and the dequantiser give
+    each tile a workgroup and launch at most 2^22 of them at a time.  2^21 + 3
+    K tiles and 2^21 + 3 V tiles at head_dim 64 (K4V2, 5 iterations) go out in
+    two launches of each kernel, the second starting at V tile 2^21 - 3.  The
+    tiles on both sides of that boundary and the first and last tile of each
+    tensor are checked against the oracle.  Inputs are normal fp16 values; the
+    dequantiser reads oracle-packed bytes at the checked tiles (written into
+    the packed arrays over the GPU's), the GPU's elsewhere."""
+    d0, n, bits = 64, (1 << 21) + 3, {True: 4, False: 2}
+    first_v2 = (1 << 22) - n                              # first V tile of the second launch
+    picks = {True: [0, 1, n - 2, n - 1],
+             False: [0, first_v2 - 2, first_v2 - 1, first_v2, first_v2 + 1, n - 1]}
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    k = torch.randn((n, 128, d0), generator=gen, device=DEV, dtype=torch.float16)
+    v = torch.randn((n, 128, d0), generator=gen, device=DEV, dtype=torch.float16)
+    xs = {True: _host(k[picks[True]]), False: _host(v[picks[False]])}
+    kc, vc, km, vm = kv.quantize_tiles(k, v, k_bits=4, v_bits=2, n_iters=5)
+    torch.cuda.synchronize()
+    D = oracle.padded_dim(d0)
+    packed = {True: (kc, km), False: (vc, vm)}
+    for is_key in (True, False):
+        c, m = packed[is_key]
+        idx = picks[is_key]
+        q = oracle.quantize_tiles(xs[is_key], bits[is_key], 5, is_key, diag=True)
+        record("launch chunks, quantize %s tiles %s" % ("K" if is_key else "V", idx),
+               compare_codes(_host(c[idx]), q, D, bits[is_key], is_key))
+        compare_meta(_host(m[idx]), q["meta"], D, is_key)
+        # the oracle's packed bytes at the checked tiles, for the dequantiser
+        c[idx] = torch.from_numpy(q["codes"]).to(DEV)
+        m[idx] = torch.from_numpy(q["meta"]).to(DEV)
+        packed[is_key] = (c, m, q)
+    kv.dequantize_tiles(kc, vc, km, vm, head_dim=d0, out=(k, v))
+    torch.cuda.synchronize()
+    for is_key, out in ((True, k), (False, v)):
+        _, _, q = packed[is_key]
+        ref, _ = oracle.dequantize_tiles(q["codes"], q["meta"], d0, bits[is_key], is_key)
+        record("launch chunks, dequantize %s" % ("K" if is_key else "V"),
+               compare_dequant(_host(out[picks[is_key]]), ref))
+    del k, v, kc, vc, km, vm
     _free()
