@@ -324,8 +324,7 @@ def stream_reference(dev, units, reps=5):
     dequantize mix also phased kernels that read 4 or 8 units before writing
     them) and grid shapes: persistent grids of 4, 8 and 16 workgroups per CU,
     and grids with one workgroup per unit in address order, the unit a tile
-    pair, a single tile (half the words) or a sixteenth of a pair (4 KB of
-    fp16).  `variants` keeps every layout's
+    pair (64 KB of fp16) or 1/2, 1/4, 1/8, 1/16 or 1/32 of one.  `variants` keeps every layout's
     best rate and `grids` the grid shape it was reached with; `by_grid_GBps`
     the best rate of each grid shape over the layouts.  `fp16_write` is
     the dequantiser's output alone (write-only, the same 4.3 GB)."""
@@ -354,8 +353,9 @@ def stream_reference(dev, units, reps=5):
         # (label, units, rq, wq, workgroups)
         grids = [("%d_per_cu" % k, units, rq, wq, cus * k) for k in (4, 8, 16)]
         grids.append(("one_per_tile_pair", units, rq, wq, units))
-        grids.append(("one_per_tile", 2 * units, rq // 2, wq // 2, 2 * units))
-        grids.append(("one_per_16th_pair", 16 * units, rq // 16, wq // 16, 16 * units))
+        for div, label in ((2, "one_per_tile"), (4, "one_per_quarter_pair"), (8, "one_per_8th_pair"),
+                           (16, "one_per_16th_pair"), (32, "one_per_32nd_pair")):
+            grids.append((label, div * units, rq // div, wq // div, div * units))
         variants, shapes, by_grid = {}, {}, {}
         for unrolled in kinds:
             best = None
