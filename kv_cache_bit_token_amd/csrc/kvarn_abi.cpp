@@ -406,8 +406,7 @@ kvarn_status kvarn_decode_attention_fp16_workspace(int32_t head_dim, int32_t bat
     int D = 0;
     kvarn_status st = check_fp16_attention(head_dim, batch, n_q_heads, n_kv_heads, seq_len, &D);
     if (st != KVARN_OK) return st;
-    int ns = 0, sps = 0;
-    kvarn::attention_fp16_plan(batch, n_kv_heads, seq_len, D, &ns, &sps);
+    const int ns = kvarn::attention_fp16_splits(batch, n_kv_heads, seq_len, D);
     *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns);
     return KVARN_OK;
 }
@@ -425,8 +424,7 @@ kvarn_status kvarn_decode_attention_fp16(int32_t head_dim, int32_t batch, int32_
     if (misaligned(q_fp16) || misaligned(out) || misaligned(k_fp16) || misaligned(v_fp16) ||
         misaligned(workspace))
         return KVARN_E_ALIGN;
-    int ns = 0, sps = 0;
-    kvarn::attention_fp16_plan(batch, n_kv_heads, seq_len, D, &ns, &sps);
+    const int ns = kvarn::attention_fp16_splits(batch, n_kv_heads, seq_len, D);
     if (ns > 0 && workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns))
         return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
@@ -442,7 +440,6 @@ kvarn_status kvarn_decode_attention_fp16(int32_t head_dim, int32_t batch, int32_
     a.n_kv_heads = n_kv_heads;
     a.seq_len = seq_len;
     a.n_splits = ns;
-    a.steps_per_split = sps;
     a.d0 = head_dim;
     a.sm_scale = sm_scale;
     hipError_t e = kvarn::launch_attention_fp16(a, D, static_cast<hipStream_t>(stream));

@@ -9,9 +9,10 @@
 //
 //   out[b][h] = softmax(sm_scale * q[b][h] . K[b][g]^T) V[b][g]
 //
-// Work split: each wavefront owns one split (a run of token steps) of one
-// (b, KV head) and every query head of its GQA group; waves never
-// synchronise and use no LDS.  A step is TS = 32 * 128 / D tokens, so K and
+// Work split: each wavefront owns one split of one (b, KV head) and every
+// query head of its GQA group; split s of n takes token steps s, s + n,
+// s + 2n, ..., so the n waves of a sequence read neighbouring steps at a
+// time.  Waves never synchronise and use no LDS.  A step is TS = 32 * 128 / D tokens, so K and
 // V of one step are 128 bytes per lane each.
 //
 // Matrix cores, v_mfma_f32_16x16x16_f16 (lane l: row / column l % 16,
@@ -44,7 +45,10 @@ namespace {
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kFp16TargetWaves = 8192;
+// Splits in total: about two per SIMD.  With strided splits this measured
+// fastest on the 64 x 8 x 16384 and 64 x 8 x 32768 caches (four splits per
+// sequence); 6, 8 or 12 splits per sequence were 4-20 % slower.
+constexpr int kFp16TargetWaves = 2048;
 constexpr float kLog2eF = 1.4426950408889634f;
 
 template <int D>
@@ -82,8 +86,10 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int64_t T = a.seq_len;
     const int64_t nsteps = (T + TS - 1) / TS;
-    const int64_t s0 = (int64_t)split * a.steps_per_split;
-    const int64_t s1 = min(s0 + (int64_t)a.steps_per_split, nsteps);
+    // strided splits: the k-th step of split s is step s + k * n_splits
+    const int64_t s0 = 0;
+    const int64_t s1 = split < nsteps ? (nsteps - split + a.n_splits - 1) / a.n_splits : 0;
+    auto step_of = [&](int64_t k) { return (int64_t)split + (k < s1 ? k : s1 - 1) * a.n_splits; };
     auto part = [&](int n) {
         return a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_splits + split) * (D + 2);
     };
@@ -126,9 +132,8 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     const int vvo = 4 * mgrp * rowb + 2 * VCPL * mrow;
     uint4 kr[NMB][NCH];
     uint32_t vr[NMB][4][VW];
-    auto load_k = [&](int64_t st) {
-        st = st < s1 ? st : s1 - 1;
-        const int64_t r0 = st * TS;
+    auto load_k = [&](int64_t k) {
+        const int64_t r0 = step_of(k) * TS;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + r0 * d0, (uint32_t)((T - r0) * rowb));
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
@@ -137,9 +142,8 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
                 kr[mb][c] = buf_load16<kPolicyNT>(r, kvo + 16 * mb * rowb + 64 * c, 0);
         }
     };
-    auto load_v = [&](int64_t st) {
-        st = st < s1 ? st : s1 - 1;
-        const int64_t r0 = st * TS;
+    auto load_v = [&](int64_t k) {
+        const int64_t r0 = step_of(k) * TS;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(vbase + r0 * d0, (uint32_t)((T - r0) * rowb));
 #pragma unroll
         for (int kb2 = 0; kb2 < NMB; ++kb2) {
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     load_v(s0);
     for (int64_t st = s0; st < s1; ++st) {
         // ---- scores (tokens past the sequence end masked) ----
-        const int rem = (int)min(T - st * TS, (int64_t)TS);
+        const int rem = (int)min(T - step_of(st) * TS, (int64_t)TS);
         float s[NMB][4];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
@@ -306,22 +310,16 @@ hipError_t launch_f16(const Fp16AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-void attention_fp16_plan(int batch, int n_kv_heads, int64_t seq_len, int D, int* n_splits,
-                         int* steps_per_split) {
+int attention_fp16_splits(int batch, int n_kv_heads, int64_t seq_len, int D) {
     const int64_t ts = 32 * 128 / D;
     const int64_t nsteps = seq_len > 0 ? (seq_len + ts - 1) / ts : 0;
     const int64_t pairs = (int64_t)batch * n_kv_heads;
-    if (nsteps == 0 || pairs == 0) {
-        *n_splits = 0;
-        *steps_per_split = 0;
-        return;
-    }
+    if (nsteps == 0 || pairs == 0) return 0;
     int64_t want = (kFp16TargetWaves + pairs - 1) / pairs;
     if (want > nsteps) want = nsteps;
     if (want < 1) want = 1;
-    const int64_t sps = (nsteps + want - 1) / want;
-    *steps_per_split = (int)sps;
-    *n_splits = (int)((nsteps + sps - 1) / sps);
+    const int64_t per = (nsteps + want - 1) / want;
+    return (int)((nsteps + per - 1) / per);
 }
 
 hipError_t launch_attention_fp16(const Fp16AttnArgs& a, int D, hipStream_t s) {

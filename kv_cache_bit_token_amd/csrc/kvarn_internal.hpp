@@ -80,8 +80,7 @@ struct Fp16AttnArgs {
     int n_q_heads;
     int n_kv_heads;
     int64_t seq_len;
-    int n_splits;        // splits per (b, g)
-    int steps_per_split; // token steps per split
+    int n_splits;        // splits per (b, g); split s takes token steps s, s + n_splits, ...
     int d0;
     float sm_scale;
 };
@@ -102,9 +101,9 @@ size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 // Packed-cache attention: the split partials, then the rotated queries.
 size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 
-// Split plan of the fp16-cache attention (token steps of 32 * 128 / D).
-void attention_fp16_plan(int batch, int n_kv_heads, int64_t seq_len, int D, int* n_splits,
-                         int* steps_per_split);
+// Splits per (b, KV head) of the fp16-cache attention (token steps of
+// 32 * 128 / D).
+int attention_fp16_splits(int batch, int n_kv_heads, int64_t seq_len, int D);
 hipError_t launch_attention_fp16(const Fp16AttnArgs& a, int D, hipStream_t s);
 
 }  // namespace kvarn
