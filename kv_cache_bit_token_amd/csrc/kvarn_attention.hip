@@ -63,12 +63,11 @@ namespace kvarn {
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-// Splits in total: about two per SIMD, one round of resident waves.  With
-// strided splits this measured fastest on the 64 x 8 x 16384 and
-// 64 x 8 x 32768 caches and the paged one (four splits per sequence, which
-// divide their tile counts evenly): eight per sequence were 1-3 % slower,
-// 7, 9, 10 or 12 per sequence 3-10 % slower than eight, two 40 % slower.
-constexpr int kTargetWaves = 2048;
+// Splits in total: about four per SIMD.  With strided splits this measured
+// fastest on the 64 x 8 x 16384 and 64 x 8 x 32768 caches (eight splits per
+// sequence, which divide their 128 and 256 tiles evenly); 7, 9, 10 or 12
+// splits per sequence were 3-10 % slower.
+constexpr int kTargetWaves = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Splits per (b, KV head): about kTargetWaves in total, at most one per tile,

@@ -124,10 +124,10 @@ def test_attention_empty_cache_is_zero():
     assert not out.cpu().numpy().any()
 
 
-@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(128, 8, 32, 13, 128), (256, 4, 32, 9, 64)])
+@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(256, 8, 32, 13, 128), (512, 4, 32, 9, 64)])
 def test_attention_several_tiles_per_split(B, n_kv, Hq, tps, d0):
     """Enough (sequence, KV head) pairs that each split runs several tiles
-    (1024 pairs -> 2 splits per pair, split s taking every other tile from
+    (2048 pairs -> 2 splits per pair, split s taking every other tile from
     tile s: 7 + 6 and 5 + 4 tiles), so the online softmax rescales across a
     split's tiles, the next-tile prefetch runs inside a split, and the combine
     merges interleaved splits.  The cache is assembled from 256 oracle-quantised tiles of
