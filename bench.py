@@ -75,44 +75,44 @@ def quant_ops_per_elem(D, n_iters):
 # decode_attention sums the query rotation, the split partials and the
 # combine; fp16_decode_attention its partials and combine.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 4295665558,
+    ("quantize", "prefill"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 4295683606,
                               "write_bytes": 905969664},
-    ("dequantize", "prefill"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 906530883,
-                                "write_bytes": 4295021504},
-    ("decode_attention", "prefill"): {"source_sha256": "d0287558aac26105", "fetch_bytes": 917365886,
-                                      "write_bytes": 10617376},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 1812082596,
-                                              "write_bytes": 8590379008},
-    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 67458968,
+    ("dequantize", "prefill"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 906533699,
+                                "write_bytes": 4295063424},
+    ("decode_attention", "prefill"): {"source_sha256": "2644352bbf86c44f", "fetch_bytes": 917369086,
+                                      "write_bytes": 10616992},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 1812083620,
+                                              "write_bytes": 8590462976},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 67459224,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 15129146,
-                                            "write_bytes": 67117184},
-    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 67458840,
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 15129146,
+                                            "write_bytes": 67110784},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 67458584,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 15129146,
-                                            "write_bytes": 67121408},
-    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 101040297,
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 15129146,
+                                            "write_bytes": 67119872},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 101040297,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 101040297,
+    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 101040169,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 268855934,
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 268855422,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 55275910,
-                                             "write_bytes": 268496832},
-    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "b43f3bb06b053ef7", "fetch_bytes": 268855038,
-                                           "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "a65b400a13816685", "fetch_bytes": 55275910,
-                                             "write_bytes": 268520128},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "d0287558aac26105", "fetch_bytes": 1823291092,
-                                                          "write_bytes": 10642400},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "c199b82bdd2de962", "fetch_bytes": 4712029131,
-                                           "write_bytes": 18116832},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "c199b82bdd2de962", "fetch_bytes": 9296548359,
-                                                               "write_bytes": 18144608},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 55275910,
+                                             "write_bytes": 268469312},
+    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 268855038,
+                                           "write_bytes": 55050624},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 55275910,
+                                             "write_bytes": 268493952},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "2644352bbf86c44f", "fetch_bytes": 1823289812,
+                                                          "write_bytes": 10642432},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "9813c8ebd5010187", "fetch_bytes": 4551330464,
+                                           "write_bytes": 5312256},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "9813c8ebd5010187", "fetch_bytes": 9109778026,
+                                                               "write_bytes": 5312928},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {
