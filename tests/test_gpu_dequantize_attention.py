@@ -65,6 +65,25 @@ def test_dequantize_random_packed(d0):
     print(compare_dequant(ko, rk), compare_dequant(vo, rv))
 
 
+
+@pytest.mark.parametrize("d0,kb,vb", [(128, 4, 2), (96, 2, 4), (256, 4, 4)])
+def test_dequantize_skipping_one_tensor(d0, kb, vb):
+    """K alone and V alone give the same bytes as both in one call: the grid
+    then covers only the tensor given, and every tile is dequantised by a
+    workgroup of its own either way."""
+    _, _, qk, qv = _oracle_cache(9, 2, 384, d0, kb, vb)
+    kc, vc, km, vm = (_cuda(x) for x in (qk["codes"], qv["codes"], qk["meta"], qv["meta"]))
+    ko, vo = kv.dequantize_tiles(kc, vc, km, vm, head_dim=d0, k_bits=kb, v_bits=vb)
+    ko1, none_v = kv.dequantize_tiles(kc, None, km, None, head_dim=d0, k_bits=kb, v_bits=vb)
+    none_k, vo1 = kv.dequantize_tiles(None, vc, None, vm, head_dim=d0, k_bits=kb, v_bits=vb)
+    torch.cuda.synchronize()
+    assert none_v is None and none_k is None
+    assert torch.equal(ko, ko1) and torch.equal(vo, vo1)
+    rk, _ = oracle.dequantize_tiles(qk["codes"], qk["meta"], d0, kb, True)
+    rv, _ = oracle.dequantize_tiles(qv["codes"], qv["meta"], d0, vb, False)
+    record("dequantize one tensor at a time %s" % ((d0, kb, vb),),
+           {"k": compare_dequant(ko1.cpu().numpy(), rk), "v": compare_dequant(vo1.cpu().numpy(), rv)})
+
 def _attention_case(B, n_kv, Hq, T, d0, seed, kb=4, vb=2):
     k, v, qk, qv = _oracle_cache(seed, B * n_kv, T, d0, kb, vb)
     q = synthetic.query_host(seed, B, Hq, d0)
