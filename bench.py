@@ -72,47 +72,47 @@ def quant_ops_per_elem(D, n_iters):
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
 # each with the SHA-256 prefix of the kernel's sources it was taken for.
-# decode_attention sums the query rotation, the split partials and the
-# combine; fp16_decode_attention its partials and combine.
+# decode_attention sums its two kernels (split partials, combine), and so
+# does fp16_decode_attention.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 4295683606,
+    ("quantize", "prefill"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 4295663894,
                               "write_bytes": 905969664},
-    ("dequantize", "prefill"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 906533699,
-                                "write_bytes": 4295063424},
-    ("decode_attention", "prefill"): {"source_sha256": "2644352bbf86c44f", "fetch_bytes": 917369086,
-                                      "write_bytes": 10616992},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 1812083620,
-                                              "write_bytes": 8590462976},
-    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 67459224,
+    ("dequantize", "prefill"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 906527939,
+                                "write_bytes": 4295080576},
+    ("decode_attention", "prefill"): {"source_sha256": "df01fb619cf2bd95", "fetch_bytes": 915822509,
+                                      "write_bytes": 9568256},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 1812083108,
+                                              "write_bytes": 8590384640},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67459096,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 15129146,
-                                            "write_bytes": 67110784},
-    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 67458584,
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 15129146,
+                                            "write_bytes": 67114112},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67458712,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 15129146,
-                                            "write_bytes": 67119872},
-    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 101040297,
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 15129146,
+                                            "write_bytes": 67115456},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040425,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 101040169,
+    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040169,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 28594342,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 268855422,
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855550,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 55275910,
-                                             "write_bytes": 268469312},
-    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "f874b1db522ae7e2", "fetch_bytes": 268855038,
-                                           "write_bytes": 55050624},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "1b2d724c7569ff59", "fetch_bytes": 55275910,
-                                             "write_bytes": 268493952},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "2644352bbf86c44f", "fetch_bytes": 1823289812,
-                                                          "write_bytes": 10642432},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "9813c8ebd5010187", "fetch_bytes": 4551330464,
-                                           "write_bytes": 5312256},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "9813c8ebd5010187", "fetch_bytes": 9109778026,
-                                                               "write_bytes": 5312928},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 55275910,
+                                             "write_bytes": 268463424},
+    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855038,
+                                           "write_bytes": 55050240},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 55275910,
+                                             "write_bytes": 268477120},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "df01fb619cf2bd95", "fetch_bytes": 1821735554,
+                                                          "write_bytes": 9590336},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 4552641401,
+                                           "write_bytes": 5311456},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 9109677805,
+                                                               "write_bytes": 5311936},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

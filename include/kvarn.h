@@ -157,8 +157,8 @@ kvarn_status kvarn_decode_attention(const kvarn_params *params, int32_t batch,
  * per GPU, held until the process ends. */
 #define KVARN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
-/* kvarn_decode_attention with its split partials and rotated queries in the
- * library's static scratch instead of a caller workspace; arguments and
+/* kvarn_decode_attention with its split partials in the library's static
+ * scratch instead of a caller workspace; arguments and
  * results are those of kvarn_decode_attention.  It allocates nothing: the
  * scratch of the current device is looked up once per device (the stream
  * must belong to the current device).  A shape whose workspace

@@ -184,7 +184,7 @@ kvarn_status kvarn_decode_attention_workspace(const kvarn_params* params, int32_
     st = check_attention_shape(batch, n_q_heads, n_kv_heads, tiles_per_seq);
     if (st != KVARN_OK) return st;
     const int ns = kvarn::attention_splits(batch, n_kv_heads, tiles_per_seq);
-    *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
+    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns);
     return KVARN_OK;
 }
 
@@ -212,7 +212,7 @@ kvarn_status decode_attention_impl(const kvarn_params* params, int32_t batch, in
         misaligned(k_meta) || misaligned(v_meta) || misaligned(workspace))
         return KVARN_E_ALIGN;
     const int ns = kvarn::attention_splits(batch, n_kv_heads, tiles_per_seq);
-    const size_t need = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns);
+    const size_t need = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns);
     if (use_static) workspace_bytes = kvarn::kStaticScratchBytes;
     if (tiles_per_seq > 0 && workspace_bytes < need) return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
@@ -314,7 +314,7 @@ kvarn_status kvarn_decode_attention_paged_workspace(const kvarn_params* params, 
     if (st != KVARN_OK) return st;
     int ns = kvarn::attention_splits(batch, n_kv_heads, max_blocks);
     if (max_blocks == 0) ns = 0;
-    *bytes = kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
+    *bytes = kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1);
     return KVARN_OK;
 }
 
@@ -346,7 +346,7 @@ kvarn_status kvarn_decode_attention_paged(const kvarn_params* params, int32_t ba
         return KVARN_E_ALIGN;
     int ns = kvarn::attention_splits(batch, n_kv_heads, max_blocks);
     if (max_blocks == 0) ns = 0;
-    if (workspace_bytes < kvarn::packed_attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
+    if (workspace_bytes < kvarn::attention_workspace_bytes(batch, n_q_heads, D, ns + 1))
         return KVARN_E_WORKSPACE;
     if (batch == 0) return KVARN_OK;
 

@@ -8,7 +8,7 @@
 //
 // Everything runs in the rotated domain; nothing is dequantised to memory.
 // With mk = 2^(k_bits-1), mv = 2^(v_bits-1):
-//   qh  = H q / sqrt(D)                          once per (b, query head)
+//   qh  = H q / sqrt(D)                          per (b, query head), in each split's wave
 //   s_t = sm * RK_t * ( sum_j (qh_j SK_j)(code_tj - mk) + sum_j qh_j (ZK_j + mk SK_j) )
 //   online softmax over the tiles of a split
 //   acc_j = CV_j * ( sum_t (p_t SV_t)(code_tj - mv) + sum_t p_t (ZV_t + mv SV_t) )
@@ -69,6 +69,8 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 // splits per sequence were 3-10 % slower.
 constexpr int kTargetWaves = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
+// The combine kernel reads at most this many parts per (b, head) in one round trip.
+constexpr int kCombineParts = 16;
 
 // Splits per (b, KV head): about kTargetWaves in total, at most one per tile,
 // and no more than the tile count needs at that many tiles per split.
@@ -84,15 +86,6 @@ int attention_splits(int batch, int n_kv_heads, int tiles_per_seq) {
 
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
     return (size_t)batch * n_q_heads * n_parts * (D + 2) * sizeof(float);
-}
-
-// byte offset of the rotated queries: the partials rounded up to 256 bytes
-static size_t qrot_offset(int batch, int n_q_heads, int D, int n_parts) {
-    return (attention_workspace_bytes(batch, n_q_heads, D, n_parts) + 255) & ~(size_t)255;
-}
-
-size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts) {
-    return qrot_offset(batch, n_q_heads, D, n_parts) + (size_t)batch * n_q_heads * D * sizeof(float);
 }
 
 // ---- packed codes -> centred bytes for the int8 matrix cores ----------------
@@ -268,25 +261,28 @@ __device__ __forceinline__ void wave_fwht(float (&v)[D / 64]) {
     for (int c = 0; c < CPL; ++c) v[c] *= sc;
 }
 
-// Rotated query of one (b, query head): H q / sqrt(D) over the padded width,
-// once per head for every split that reads it.  One wavefront per head, four
-// heads per workgroup.
-template <int D>
-__global__ __launch_bounds__(256) void attn_rotate_q_kernel(AttnArgs a) {
-    constexpr int CPL = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);   // b * n_q_heads + h
-    if (bh >= a.batch * a.n_q_heads) return;
-    float v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int j = CPL * lane + c;
-        v[c] = (j < a.d0) ? h2f_bits(a.q[(size_t)bh * a.d0 + j]) : 0.0f;
+// CPL consecutive fp16 channels of a query row as one load, and their floats.
+template <int CPL> struct QRowChunk;
+template <> struct QRowChunk<1> {
+    using type = uint16_t;
+    __device__ static void unpack(type w, float (&v)[1]) { v[0] = h2f_bits(w); }
+};
+template <> struct QRowChunk<2> {
+    using type = uint32_t;
+    __device__ static void unpack(type w, float (&v)[2]) {
+        v[0] = h2f_bits((uint16_t)w);
+        v[1] = h2f_bits((uint16_t)(w >> 16));
     }
-    wave_fwht<D>(v);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) a.qrot[(size_t)bh * D + CPL * lane + c] = v[c];
-}
+};
+template <> struct QRowChunk<4> {
+    using type = uint2;
+    __device__ static void unpack(type w, float (&v)[4]) {
+        v[0] = h2f_bits((uint16_t)w.x);
+        v[1] = h2f_bits((uint16_t)(w.x >> 16));
+        v[2] = h2f_bits((uint16_t)w.y);
+        v[3] = h2f_bits((uint16_t)(w.y >> 16));
+    }
+};
 
 template <int D, int GM>
 __device__ void attn_tail_block(const AttnArgs& a, int bg, uint8_t* lds);
@@ -432,29 +428,23 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             mt[r] = *src;
         }
     };
-    // q' tasks: task t = lane + 64 r covers head n = t / QPH and the 4
-    // channels of dword j of run (lane group gq, chunk kc):
-    //   channel gq D/4 + 16 kc + base(j) + stride n', n' = 0..3
-    // The group's rotated queries (H q / sqrt(D), from the rotation kernel)
-    // at those channels, and then the first tile, go out before anything waits.
-    float qh[QR][4];
-#pragma unroll
-    for (int r = 0; r < QR; ++r) {
-        const int t = lane + 64 * r;
-        const int n = t / QPH, rem = t % QPH;
-        const int gq = rem / (D / 16), rem2 = rem % (D / 16);
-        const int kc = rem2 >> 2, j = rem2 & 3;
-        const bool live = n < G;
-        const float* src = a.qrot + ((size_t)b * a.n_q_heads + g * G + (live ? n : 0)) * D;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ch = gq * (D / 4) + 16 * kc + RunOrder<KB>::base(j) + RunOrder<KB>::kStride * e;
-            qh[r][e] = live ? src[ch] : 0.0f;
-        }
-    }
+    // The first tile, then the group's fp16 queries, go out before anything
+    // waits.  A query row is read in the layout of wave_fwht (lane l holds
+    // channels CPL l .. CPL l + CPL - 1, zero past head_dim; head_dim is a
+    // multiple of 8, so no lane straddles it).
     load_meta(t0);
     load_k(t0);
     load_v(t0);
+    constexpr int CPL = D / 64;
+    using QRaw = typename QRowChunk<CPL>::type;
+    QRaw qraw[GMAX];
+    {
+        const uint16_t* qg = a.q + ((size_t)b * a.n_q_heads + g * G) * a.d0 + CPL * lane;
+        const bool in_row = CPL * lane < a.d0;
+#pragma unroll
+        for (int n = 0; n < GMAX; ++n)
+            qraw[n] = (n < G && in_row) ? *reinterpret_cast<const QRaw*>(qg + (size_t)n * a.d0) : QRaw{};
+    }
 
     // softmax state and accumulator of head 4 rb + lgr (channel 16 nb + col)
     float m_run[RBMAX], l_run[RBMAX];
@@ -466,7 +456,43 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NNB; ++nb) acc[rb][nb] = 0.0f;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile, once
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile and the queries, once
+
+    // Rotated queries H q / sqrt(D) of the group, one transform per head,
+    // staged as floats [G][D] in the q' image region (G D 4 bytes fit in its
+    // ceil(G / 4) 16 D bytes; the first tile's q' digits overwrite them only
+    // after the gather below).  q' tasks: task t = lane + 64 r covers head
+    // n = t / QPH and the 4 channels of dword j of run (lane group gq, chunk kc):
+    //   channel gq D/4 + 16 kc + base(j) + stride n', n' = 0..3
+    float qh[QR][4];
+    {
+        float* qst = reinterpret_cast<float*>(qaimg);
+#pragma unroll
+        for (int n = 0; n < GMAX; ++n) {
+            if (n < G) {
+                float v[CPL];
+                QRowChunk<CPL>::unpack(qraw[n], v);
+                wave_fwht<D>(v);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) qst[n * D + CPL * lane + c] = v[c];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const int t = lane + 64 * r;
+            const int n = t / QPH, rem = t % QPH;
+            const int gq = rem / (D / 16), rem2 = rem % (D / 16);
+            const int kc = rem2 >> 2, j = rem2 & 3;
+            const bool live = n < G;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ch = gq * (D / 4) + 16 * kc + RunOrder<KB>::base(j) + RunOrder<KB>::kStride * e;
+                qh[r][e] = live ? qst[(live ? n : 0) * D + ch] : 0.0f;   // index kept inside the image
+            }
+        }
+        wave_sync();
+    }
 
     for (int ti = t0; ti < t1; ++ti) {
         // ---- meta of the tile into the wave's LDS, then the next tile's meta ----
@@ -666,36 +692,65 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);   // b * n_q_heads + h
     if (bh >= a.batch * a.n_q_heads) return;
     const float* p = a.ws + (size_t)bh * a.n_parts * (D + 2);
-    // global max and the normaliser over the parts (lanes stride the parts)
-    float M = -INFINITY;
-    for (int s = lane; s < a.n_parts; s += 64) M = fmaxf(M, p[(size_t)s * (D + 2)]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    // the normaliser and the weighted sum of the parts' accumulators, CPL
-    // channels per lane.  In each chunk of 64 parts, lane k computes part
-    // k's weight and the loop reads it back lane by lane, so that the
-    // accumulator loads of successive parts do not wait on one another.
-    float L = 0.0f;
+    float M = -INFINITY, L = 0.0f;
     float v[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) v[c] = 0.0f;
-    for (int base = 0; base < a.n_parts; base += 64) {
-        const int s = base + lane;
-        float w = 0.0f;
-        if (s < a.n_parts) {
-            const float ms = p[(size_t)s * (D + 2)];
-            if (ms != -INFINITY) {
-                w = exp2f((ms - M) * kLog2e);
-                L += p[(size_t)s * (D + 2) + 1] * w;
-            }
+    if (a.n_parts <= kCombineParts) {
+        // Few parts: every load goes out at once (lane s: part s's max and
+        // sum; every lane: its CPL channels of each part's accumulator), so
+        // the wave waits on memory once.  Same sums, in the same order, as
+        // the general path below.
+        float ms = -INFINITY, ls = 0.0f;
+        if (lane < a.n_parts) {
+            ms = p[(size_t)lane * (D + 2)];
+            ls = p[(size_t)lane * (D + 2) + 1];
         }
-        const int cnt = min(64, a.n_parts - base);
-        const float* pb = p + (size_t)base * (D + 2) + 2 + CPL * lane;
-#pragma unroll 4
-        for (int k = 0; k < cnt; ++k) {
+        float pv[kCombineParts][CPL];
+#pragma unroll
+        for (int k = 0; k < kCombineParts; ++k)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                pv[k][c] = k < a.n_parts ? p[(size_t)(k < a.n_parts ? k : 0) * (D + 2) + 2 + CPL * lane + c]
+                                         : 0.0f;   // the address stays inside this head's parts
+        M = ms;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float w = (ms != -INFINITY) ? exp2f((ms - M) * kLog2e) : 0.0f;
+        L = ls * w;
+#pragma unroll
+        for (int k = 0; k < kCombineParts; ++k) {
             const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(pb[(size_t)k * (D + 2) + c], wk, v[c]);
+            for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(pv[k][c], wk, v[c]);
+        }
+    } else {
+        // global max over the parts (lanes stride the parts)
+        for (int s = lane; s < a.n_parts; s += 64) M = fmaxf(M, p[(size_t)s * (D + 2)]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        // the normaliser and the weighted sum of the parts' accumulators, CPL
+        // channels per lane.  In each chunk of 64 parts, lane k computes part
+        // k's weight and the loop reads it back lane by lane, so that the
+        // accumulator loads of successive parts do not wait on one another.
+        for (int base = 0; base < a.n_parts; base += 64) {
+            const int s = base + lane;
+            float w = 0.0f;
+            if (s < a.n_parts) {
+                const float ms = p[(size_t)s * (D + 2)];
+                if (ms != -INFINITY) {
+                    w = exp2f((ms - M) * kLog2e);
+                    L += p[(size_t)s * (D + 2) + 1] * w;
+                }
+            }
+            const int cnt = min(64, a.n_parts - base);
+            const float* pb = p + (size_t)base * (D + 2) + 2 + CPL * lane;
+#pragma unroll 4
+            for (int k = 0; k < cnt; ++k) {
+                const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(pb[(size_t)k * (D + 2) + c], wk, v[c]);
+            }
         }
     }
 #pragma unroll
@@ -904,13 +959,6 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
     AttnArgs a = args;
     const int G = a.n_q_heads / a.n_kv_heads;
     if (a.n_splits > 0) {
-        // the rotated queries follow the split partials in the workspace
-        a.qrot = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) +
-                                          qrot_offset(a.batch, a.n_q_heads, D, a.n_parts));
-        hipLaunchKernelGGL((attn_rotate_q_kernel<D>), dim3((unsigned)((a.batch * a.n_q_heads + 3) / 4)),
-                           dim3(256), 0, s, a);
-        hipError_t e0 = hipGetLastError();
-        if (e0 != hipSuccess) return e0;
         const int per_wave = AttnLds<D>::bytes(G);
         int wpb = 65536 / per_wave;
         if (wpb > 4) wpb = 4;

@@ -66,7 +66,6 @@ struct AttnArgs {
     const uint16_t* v_tail = nullptr;
     int tail_in_grid = 0;               // set by the launcher: tails run as extra partial-kernel blocks
     int64_t pool_blocks = 0;
-    float* qrot = nullptr;              // [B][Hq][D] rotated queries (set by the launcher)
 };
 
 // Decode attention over an uncompressed fp16 cache (the baseline).
@@ -97,9 +96,8 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kb, int vb, hipStream_
 // Split-K plan of the decode attention for a shape (shared by the workspace
 // query and the launch, so both agree).
 int attention_splits(int batch, int n_kv_heads, int tiles_per_seq);
+// Split partials [batch][n_q_heads][n_parts][D + 2] (max, sum, accumulator).
 size_t attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
-// Packed-cache attention: the split partials, then the rotated queries.
-size_t packed_attention_workspace_bytes(int batch, int n_q_heads, int D, int n_parts);
 
 // Splits per (b, KV head) of the fp16-cache attention (token steps of
 // 32 * 128 / D).
