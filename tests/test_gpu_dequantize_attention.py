@@ -128,6 +128,19 @@ def test_attention_more_than_64_splits(B, n_kv, Hq, tiles, d0):
     record("attention, more than 64 splits %s" % ((B, n_kv, Hq, tiles, d0),), compare_attention(out, ref))
 
 
+@pytest.mark.parametrize("tiles,d0", [(16, 128), (17, 128), (16, 256), (17, 64)])
+def test_attention_combine_part_counts(tiles, d0):
+    """16 and 17 splits per head (one tile each): the combine kernel reads up
+    to 16 parts in a single round of loads and more in its loop over chunks;
+    both sides of that boundary match the oracle."""
+    wsb = kv.decode_attention_workspace(batch=1, n_q_heads=4, n_kv_heads=1, tiles_per_seq=tiles,
+                                        head_dim=d0)
+    D = oracle.padded_dim(d0)
+    assert wsb == 4 * tiles * (D + 2) * 4, "expected one split per tile"
+    out, ref = _attention_case(1, 1, 4, tiles * 128, d0, seed=tiles * 7 + d0)
+    record("attention, %d parts per head, head_dim %d" % (tiles, d0), compare_attention(out, ref))
+
+
 def test_attention_other_presets():
     for kb, vb in ((4, 4), (2, 2), (2, 4)):
         out, ref = _attention_case(1, 2, 8, 256, 128, seed=3, kb=kb, vb=vb)
