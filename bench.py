@@ -75,44 +75,44 @@ def quant_ops_per_elem(D, n_iters):
 # decode_attention sums its two kernels (split partials, combine), and so
 # does fp16_decode_attention.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 4295663894,
+    ("quantize", "prefill"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 4295733396,
                               "write_bytes": 905969664},
-    ("dequantize", "prefill"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 906527939,
-                                "write_bytes": 4295080576},
-    ("decode_attention", "prefill"): {"source_sha256": "df01fb619cf2bd95", "fetch_bytes": 915822509,
-                                      "write_bytes": 9568256},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 1812083108,
-                                              "write_bytes": 8590384640},
-    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67459096,
+    ("dequantize", "prefill"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 910014299,
+                                "write_bytes": 4295042496},
+    ("decode_attention", "prefill"): {"source_sha256": "f49eb008050e22d5", "fetch_bytes": 911031228,
+                                      "write_bytes": 5308416},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 1822921951,
+                                              "write_bytes": 8590035520},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67459480,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 15129146,
-                                            "write_bytes": 67114112},
-    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67458712,
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 15132794,
+                                            "write_bytes": 67109376},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67458840,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 15129146,
-                                            "write_bytes": 67115456},
-    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040425,
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 15134330,
+                                            "write_bytes": 67109888},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040297,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 28597798,
                                             "write_bytes": 100663296},
     ("quantize", "head_dim_96_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040169,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 28594342,
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 28597670,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855550,
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855294,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 55275910,
-                                             "write_bytes": 268463424},
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 55288901,
+                                             "write_bytes": 268440256},
     ("quantize", "head_dim_256_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855038,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "03e89231411c7454", "fetch_bytes": 55275910,
-                                             "write_bytes": 268477120},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "df01fb619cf2bd95", "fetch_bytes": 1821735554,
-                                                          "write_bytes": 9590336},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 4552641401,
-                                           "write_bytes": 5311456},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 9109677805,
-                                                               "write_bytes": 5311936},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 55292037,
+                                             "write_bytes": 268441344},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "f49eb008050e22d5", "fetch_bytes": 1816947474,
+                                                          "write_bytes": 5310240},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 4552355201,
+                                           "write_bytes": 5311520},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 9107905955,
+                                                               "write_bytes": 5312288},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

@@ -63,11 +63,12 @@ namespace kvarn {
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
-// Splits in total: about four per SIMD.  With strided splits this measured
-// fastest on the 64 x 8 x 16384 and 64 x 8 x 32768 caches (eight splits per
-// sequence, which divide their 128 and 256 tiles evenly); 7, 9, 10 or 12
-// splits per sequence were 3-10 % slower.
-constexpr int kTargetWaves = 4096;
+// Splits in total: about two per SIMD.  Timed on a cache that no earlier
+// pass has left in the last-level cache, four strided splits per sequence
+// were fastest on the 64 x 8 x 16384 cache (0.149 ms, against 0.153 at eight
+// and 0.158 at twelve); on 64 x 8 x 32768 the three counts were within the
+// run-to-run spread.  Four divide both caches' 128 and 256 tiles evenly.
+constexpr int kTargetWaves = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 // The combine kernel reads at most this many parts per (b, head) in one round trip.
 constexpr int kCombineParts = 16;

@@ -23,7 +23,8 @@
 // neighbouring token groups then take whole words of their channel rows and
 // swap bytes inside the wavefront.  (Read by each wavefront straight from
 // memory, the partly used 128-byte lines of the V rows were fetched from HBM
-// again when the cache dropped them between the wavefronts' reads.)  The
+// again when the cache dropped them between the wavefronts' reads.)  Code and
+// meta loads carry the nontemporal hint, as the output stores do.  The
 // per-token K factor RK_t and the 1/sqrt(D) scale are applied
 // after the transform (they commute with it); for V, 1/sqrt(D) is folded
 // into CV_j.
@@ -98,6 +99,24 @@ struct VBlock {
     }
 };
 
+// Global loads with the nontemporal hint: every code and meta byte is read
+// once per call.  Inside the prefill step (the cache read after the
+// quantiser's 5 GB) they took the kernel from 0.927 to 0.905 ms; the packed
+// attention's meta loads, given the same hint, were slower.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 __device__ __forceinline__ float half_of(const uint32_t* pairs, int k) {
     return h2f_bits((uint16_t)((k & 1) ? (pairs[k >> 1] >> 16) : (pairs[k >> 1] & 0xFFFF)));
 }
@@ -118,18 +137,18 @@ __device__ __forceinline__ void load_tile(Packed<D, BITS, IS_K>& p, const uint8_
     for (int k = 0; k < MP::NS; ++k) {
         int e = ln + 64 * k;
         if (e >= MP::NC) e = 0;   // spare lanes re-read chunk 0 (keeps the load unconditional)
-        p.m[k] = *reinterpret_cast<const uint4*>(meta + MP::src(e, tok0));
+        p.m[k] = ld_nt16(meta + MP::src(e, tok0));
     }
     if constexpr (IS_K) {
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             const uint8_t* src = codes + ((4 * tb + i) * D + 16 * nb) * BITS / 8;
             if constexpr (BITS == 4) {
-                const uint2 w = *reinterpret_cast<const uint2*>(src);
+                const uint2 w = ld_nt8(src);
                 p.c[i][0] = w.x;
                 p.c[i][1] = w.y;
             } else {
-                p.c[i][0] = *reinterpret_cast<const uint32_t*>(src);
+                p.c[i][0] = ld_nt4(src);
             }
         }
     } else {
@@ -137,7 +156,7 @@ __device__ __forceinline__ void load_tile(Packed<D, BITS, IS_K>& p, const uint8_
         // 1 KB of consecutive bytes
 #pragma unroll
         for (int k = 0; k < BITS / 2; ++k)
-            p.v[k] = reinterpret_cast<const uint4*>(codes)[threadIdx.x + 2 * D * k];
+            p.v[k] = ld_nt16(reinterpret_cast<const uint4*>(codes) + threadIdx.x + 2 * D * k);
     }
 }
 
@@ -320,7 +339,6 @@ __device__ __forceinline__ void dequantize_tile(const Packed<D, BITS, IS_K>& p, 
             const int g = ln + 64 * s2;
             if (!FULL && g >= run) break;
             const int r = g / CPR, ch = g % CPR;
-            using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
             __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(xch + 4 * slot(r, ch)),
                                         reinterpret_cast<u32x4*>(dst + g));
         }

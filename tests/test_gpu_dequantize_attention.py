@@ -156,16 +156,20 @@ def test_attention_empty_cache_is_zero():
     assert not out.cpu().numpy().any()
 
 
-@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(256, 8, 32, 13, 128), (512, 4, 32, 9, 64)])
+@pytest.mark.parametrize("B,n_kv,Hq,tps,d0", [(128, 8, 32, 13, 128), (256, 4, 32, 9, 64)])
 def test_attention_several_tiles_per_split(B, n_kv, Hq, tps, d0):
     """Enough (sequence, KV head) pairs that each split runs several tiles
-    (2048 pairs -> 2 splits per pair, split s taking every other tile from
+    (1024 pairs -> 2 splits per pair, split s taking every other tile from
     tile s: 7 + 6 and 5 + 4 tiles), so the online softmax rescales across a
     split's tiles, the next-tile prefetch runs inside a split, and the combine
     merges interleaved splits.  The cache is assembled from 256 oracle-quantised tiles of
     the config-1 recipe, drawn at random per position; the host checks that a
     later tile of a split often holds a head's largest score, so the running
     maximum really moves inside splits."""
+    D = oracle.padded_dim(d0)
+    wsb = kv.decode_attention_workspace(batch=B, n_q_heads=Hq, n_kv_heads=n_kv, tiles_per_seq=tps,
+                                        head_dim=d0)
+    assert wsb == B * Hq * 2 * (D + 2) * 4, "expected two splits per (sequence, KV head)"
     rng = np.random.default_rng(B + d0)
     k, v = synthetic.outlier_kv_host(B + tps, 2, 128 * 128, d0)
     kt, vt = synthetic.as_tiles(k), synthetic.as_tiles(v)      # 256 tiles each
