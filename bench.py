@@ -637,6 +637,10 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (dequantize 256x8x8192, head_dim sweep, "
                          "attention 64x8x32768), timed kernel by kernel after the step")
+    ap.add_argument("--cold-stages", action="store_true",
+                    help="fill the last-level cache with clean, unrelated lines before each stage of the "
+                         "step (outside the stage timers, inside ms_per_step), so that no stage reads "
+                         "what the previous one left cached")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--alu-classes", action="store_true",
@@ -680,21 +684,40 @@ def main():
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty((LAYERS, Q_HEADS, HEAD_DIM), dtype=torch.float32, device=dev)
 
+    if args.cold_stages:
+        # 1 GiB written (evicting and writing back whatever the 256 MB
+        # last-level cache holds), then another 1 GiB read, so that each stage
+        # starts with that cache full of clean lines of unrelated data
+        junk = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        clean = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        acc = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def between_stages():
+        if args.cold_stages:
+            junk.add_(1.0)
+            torch.sum(clean, dim=0, keepdim=True, out=acc)
+
     def step(ev=None):
+        # ev: start and end of each stage (quantise, dequantise, attention)
+        between_stages()
         if ev: ev[0].record()
         kv.quantize_tiles(kt, vt, k_bits=K_BITS, v_bits=V_BITS, n_iters=N_ITERS, out=(kc, vc, km, vm))
         if ev: ev[1].record()
+        between_stages()
+        if ev: ev[2].record()
         kv.dequantize_tiles(kc, vc, km, vm, head_dim=HEAD_DIM, k_bits=K_BITS, v_bits=V_BITS,
                             out=(ko, vo))
-        if ev: ev[2].record()
+        if ev: ev[3].record()
+        between_stages()
+        if ev: ev[4].record()
         kv.decode_attention(q, kc, vc, km, vm, n_kv_heads=KV_HEADS, tiles_per_seq=tiles_per_seq,
                             k_bits=K_BITS, v_bits=V_BITS, workspace=ws, out=out)
-        if ev: ev[3].record()
+        if ev: ev[5].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -705,7 +728,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
-    stage_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i in range(3)]
+    stage_ms = [sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in events) / args.steps for i in range(3)]
 
     b = per_tile_bytes(HEAD_DIM)
     fp16_total = n_tiles * b["fp16_pair"]              # 4.29 GB of fp16 K+V
@@ -756,7 +779,8 @@ def main():
                                    "quantise + dequantise kernel time (attention reported apart)",
                    "hbm_frac_quantize_dequantize": round((hbm["quantize"] + hbm["dequantize"])
                                                          / (qd_ms / 1e3) / HBM_PEAK, 4),
-                   "tiles": n_tiles, "kv_fp16_bytes": fp16_total, "packed_bytes": packed_total},
+                   "tiles": n_tiles, "kv_fp16_bytes": fp16_total, "packed_bytes": packed_total,
+                   "cold_stages": bool(args.cold_stages)},
         "stages": stages,
         "roofline": roofline,
         "wall_s": round(t_wall, 3),
