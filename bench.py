@@ -72,47 +72,48 @@ def quant_ops_per_elem(D, n_iters):
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (FETCH_SIZE scaled by the copy calibration), keyed by (kernel, workload),
 # each with the SHA-256 prefix of the kernel's sources it was taken for.
-# decode_attention sums its two kernels (split partials, combine), and so
-# does fp16_decode_attention.
+# decode_attention is its partial kernel, which merges the splits in the
+# workgroup on these workloads; fp16_decode_attention sums its partial and
+# combine kernels.
 TRAFFIC = {
-    ("quantize", "prefill"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 4295733396,
+    ("quantize", "prefill"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 4295693461,
                               "write_bytes": 905969664},
-    ("dequantize", "prefill"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 910014299,
-                                "write_bytes": 4295042496},
-    ("decode_attention", "prefill"): {"source_sha256": "f49eb008050e22d5", "fetch_bytes": 911031228,
-                                      "write_bytes": 5308416},
-    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 1822921951,
-                                              "write_bytes": 8590035520},
-    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67459480,
+    ("dequantize", "prefill"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 909857119,
+                                "write_bytes": 4295037888},
+    ("decode_attention", "prefill"): {"source_sha256": "23ec0f4f7f57c67e", "fetch_bytes": 906740413,
+                                      "write_bytes": 1048576},
+    ("dequantize", "dequantize_256x8x8192"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 1821906301,
+                                              "write_bytes": 8590013440},
+    ("quantize", "head_dim_64_iters_3"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 67459352,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 15132794,
-                                            "write_bytes": 67109376},
-    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 67458840,
+    ("dequantize", "head_dim_64_iters_3"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 15133818,
+                                            "write_bytes": 67109056},
+    ("quantize", "head_dim_64_iters_5"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 67458840,
                                           "write_bytes": 14942208},
-    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 15134330,
-                                            "write_bytes": 67109888},
-    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040297,
+    ("dequantize", "head_dim_64_iters_5"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 15132794,
+                                            "write_bytes": 67108864},
+    ("quantize", "head_dim_96_iters_3"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 101040425,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 28597798,
+    ("dequantize", "head_dim_96_iters_3"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 28597542,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 101040169,
+    ("quantize", "head_dim_96_iters_5"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 101040297,
                                           "write_bytes": 28311552},
-    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 28597670,
+    ("dequantize", "head_dim_96_iters_5"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 28597414,
                                             "write_bytes": 100663296},
-    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855294,
+    ("quantize", "head_dim_256_iters_3"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 268855806,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 55288901,
-                                             "write_bytes": 268440256},
-    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "27f5a36ee502d493", "fetch_bytes": 268855038,
+    ("dequantize", "head_dim_256_iters_3"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 55287429,
+                                             "write_bytes": 268435584},
+    ("quantize", "head_dim_256_iters_5"): {"source_sha256": "7fe5374b5ba8147d", "fetch_bytes": 268855038,
                                            "write_bytes": 55050240},
-    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "c60e355dbd591986", "fetch_bytes": 55292037,
-                                             "write_bytes": 268441344},
-    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "f49eb008050e22d5", "fetch_bytes": 1816947474,
-                                                          "write_bytes": 5310240},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 4552355201,
-                                           "write_bytes": 5311520},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "621acf00ba0bb5e9", "fetch_bytes": 9107905955,
-                                                               "write_bytes": 5312288},
+    ("dequantize", "head_dim_256_iters_5"): {"source_sha256": "c2af6ee1b9d5d2aa", "fetch_bytes": 55286661,
+                                             "write_bytes": 268436608},
+    ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "23ec0f4f7f57c67e", "fetch_bytes": 1812656019,
+                                                          "write_bytes": 1048576},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "288ebbc3a597656e", "fetch_bytes": 4552059914,
+                                           "write_bytes": 5311808},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "288ebbc3a597656e", "fetch_bytes": 9109560305,
+                                                               "write_bytes": 5313184},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

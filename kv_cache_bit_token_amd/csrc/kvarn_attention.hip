@@ -46,15 +46,17 @@
 // are the meta, the q' image and the p' image.
 //
 // Work split: each wavefront owns one split of one (b, KV head) and every
-// query head of that head's GQA group; these waves never synchronise with
-// each other.  Split s of n takes tiles s, s + n, s + 2n, ... of the
+// query head of that head's GQA group; these waves do not synchronise with
+// each other before their last tile.  Split s of n takes tiles s, s + n, s + 2n, ... of the
 // sequence, so the n waves of a sequence read n neighbouring tiles at a time
 // and the device reads a few hundred short windows instead of one long run
 // per wave.  A paged call's fp16 tails run as
 // extra 256-thread workgroups of the same grid where its workgroups have
 // 256 threads (they synchronise only among their own waves), else as a
-// kernel of their own.  A combine kernel merges the splits' (max, sum, acc)
-// and undoes the rotation.
+// kernel of their own.  Where a (b, KV head)'s splits fit one workgroup
+// (no block table, no tails, at most 4 splits) they run as its waves and
+// merge there, through LDS; otherwise a combine kernel merges the splits'
+// (max, sum, acc).  Either way the merge undoes the rotation.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 #include "kvarn_rsrc.hpp"
@@ -285,6 +287,51 @@ template <> struct QRowChunk<4> {
     }
 };
 
+// The splits of one (b, KV head) as the waves of one workgroup (split =
+// wave), merged there: each wave has written its (m, l, acc) per query head
+// to ex[split][n][D + 2] in LDS and passed a barrier; wave w then merges
+// heads w, w + n_splits, ... exactly as the combine kernel does (same
+// reductions, same order) and writes their outputs.
+template <int D>
+__device__ void merge_splits_in_block(const AttnArgs& a, const float* ex, int b, int g, int G, int wave) {
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int ns = a.n_splits;
+    for (int n = wave; n < G; n += ns) {
+        float ms = -INFINITY, ls = 0.0f;
+        if (lane < ns) {
+            ms = ex[((size_t)lane * G + n) * (D + 2)];
+            ls = ex[((size_t)lane * G + n) * (D + 2) + 1];
+        }
+        float M = ms;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float w = (ms != -INFINITY) ? exp2f((ms - M) * kLog2e) : 0.0f;
+        float L = ls * w;
+        float v[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = 0.0f;
+        for (int k = 0; k < ns; ++k) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+            const float* pk = ex + ((size_t)k * G + n) * (D + 2) + 2 + CPL * lane;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) v[c] = __builtin_fmaf(pk[c], wk, v[c]);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+        const float il = (L > 0.0f) ? 1.0f / L : 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] *= il;
+        wave_fwht<D>(v);
+        const size_t bh = (size_t)b * a.n_q_heads + g * G + n;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int j = CPL * lane + c;
+            if (j < a.d0) a.out[bh * a.d0 + j] = v[c];
+        }
+    }
+}
+
 template <int D, int GM>
 __device__ void attn_tail_block(const AttnArgs& a, int bg, uint8_t* lds);
 
@@ -332,10 +379,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int t1 = split < ntiles ? (ntiles - split + a.n_splits - 1) / a.n_splits : 0;
     if (t0 >= t1) {
         // nothing in this split: an empty partial (m = -inf, l = 0, acc = 0)
+        float* ex = reinterpret_cast<float*>(smem);
+        if (a.fuse_combine) __syncthreads();
         for (int k = lane; k < G * (D + 2); k += 64) {
             const int n = k / (D + 2), e = k % (D + 2);
-            float* p = a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
+            float* p = a.fuse_combine
+                ? ex + ((size_t)split * G + n) * (D + 2)
+                : a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
             p[e] = (e == 0) ? -INFINITY : 0.0f;
+        }
+        if (a.fuse_combine) {
+            __syncthreads();
+            merge_splits_in_block<D>(a, ex, b, g, G, wave);
         }
         return;
     }
@@ -669,12 +724,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         wave_sync();
     }
 
-    // ---- partial result of this split: (m, l, acc[D]) per query head ----
+    // ---- partial result of this split: (m, l, acc[D]) per query head, to
+    // the workspace, or (all splits of this (b, g) in this workgroup) to LDS
+    // once every wave is done with its own region, merged in the block ----
+    float* ex = reinterpret_cast<float*>(smem);
+    if (a.fuse_combine) __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RBMAX; ++rb) {
         const int n = 4 * rb + lgr;
         if (rb < RB && n < G) {
-            float* p = a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
+            float* p = a.fuse_combine
+                ? ex + ((size_t)split * G + n) * (D + 2)
+                : a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_parts + split) * (D + 2);
 #pragma unroll
             for (int nb = 0; nb < NNB; ++nb) p[2 + 16 * nb + col] = acc[rb][nb];
             if (col == 0) {
@@ -682,6 +743,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
                 p[1] = l_run[rb];
             }
         }
+    }
+    if (a.fuse_combine) {
+        __syncthreads();
+        merge_splits_in_block<D>(a, ex, b, g, G, wave);
     }
 }
 
@@ -964,6 +1029,16 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
         int wpb = 65536 / per_wave;
         if (wpb > 4) wpb = 4;
         if (wpb < 1) wpb = 1;
+        // Without a block table or tails, when a (b, g)'s splits fit one
+        // workgroup, they run as its waves and merge there: no combine launch
+        // and no partials in memory.  The merge's exchange, n_splits x G x
+        // (D + 2) floats, fits the waves' LDS regions (each holds the q' image
+        // of G heads, 16 D ceil(G / 4) bytes or more).
+        if (!a.table && !a.tail_len && a.n_splits <= wpb &&
+            (size_t)a.n_splits * G * (D + 2) * sizeof(float) <= (size_t)per_wave * a.n_splits) {
+            wpb = a.n_splits;
+            a.fuse_combine = 1;
+        }
         const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
         int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
         // A paged call's fp16 tails run as extra blocks of the same grid where
@@ -984,6 +1059,7 @@ static hipError_t launch_att(const AttnArgs& args, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (a.fuse_combine) return hipSuccess;
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((a.batch * a.n_q_heads + 3) / 4)),
                        dim3(256), 0, s, a);
     return hipGetLastError();

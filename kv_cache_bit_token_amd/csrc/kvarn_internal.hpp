@@ -65,6 +65,7 @@ struct AttnArgs {
     const uint16_t* k_tail = nullptr;   // [batch][n_kv_heads][128][d0]
     const uint16_t* v_tail = nullptr;
     int tail_in_grid = 0;               // set by the launcher: tails run as extra partial-kernel blocks
+    int fuse_combine = 0;               // set by the launcher: each workgroup holds all splits of one (b, g) and merges them
     int64_t pool_blocks = 0;
 };
 
