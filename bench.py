@@ -110,10 +110,10 @@ TRAFFIC = {
                                              "write_bytes": 268436608},
     ("decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "23ec0f4f7f57c67e", "fetch_bytes": 1812656019,
                                                           "write_bytes": 1048576},
-    ("fp16_decode_attention", "prefill"): {"source_sha256": "288ebbc3a597656e", "fetch_bytes": 4552059914,
-                                           "write_bytes": 5311808},
-    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "288ebbc3a597656e", "fetch_bytes": 9109560305,
-                                                               "write_bytes": 5313184},
+    ("fp16_decode_attention", "prefill"): {"source_sha256": "0fde22ebbf659794", "fetch_bytes": 4560699399,
+                                           "write_bytes": 1048576},
+    ("fp16_decode_attention", "decode_attention_64x8x32768"): {"source_sha256": "0fde22ebbf659794", "fetch_bytes": 9142235549,
+                                                               "write_bytes": 1048576},
 }
 _CSRC = os.path.join(ROOT, "kv_cache_bit_token_amd", "csrc")
 KERNEL_SOURCES = {

@@ -12,7 +12,8 @@
 // Work split: each wavefront owns one split of one (b, KV head) and every
 // query head of its GQA group; split s of n takes token steps s, s + n,
 // s + 2n, ..., so the n waves of a sequence read neighbouring steps at a
-// time.  Waves never synchronise and use no LDS.  A step is TS = 32 * 128 / D tokens, so K and
+// time.  Waves do not synchronise before their last step; only the merge
+// below uses LDS.  A step is TS = 32 * 128 / D tokens, so K and
 // V of one step are 128 bytes per lane each.
 //
 // Matrix cores, v_mfma_f32_16x16x16_f16 (lane l: row / column l % 16,
@@ -32,8 +33,9 @@
 // Loads run one step ahead: the next step's K right after this step's
 // q.K^T, its V right after this step's p.V; every load is unconditional
 // (rows past the sequence end read zero through a range-checked descriptor)
-// so each wait covers a fixed number of younger loads.  A combine kernel
-// merges the splits.
+// so each wait covers a fixed number of younger loads.  Up to four splits
+// of a (b, KV head) run as the waves of one workgroup and merge there
+// through LDS; more splits go through a combine kernel.
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 #include "kvarn_rsrc.hpp"
@@ -69,7 +71,33 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {   // {a.hi
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// The splits of one (b, KV head) as the waves of one workgroup (MERGE),
+// merged there: each wave has written its (m, l, acc) per query head to
+// ex[split][n][D + 2] in LDS and passed a barrier; the workgroup's threads
+// then form the outputs exactly as the combine kernel does (same sums, same
+// order).
 template <int D>
+__device__ void fp16_merge_in_block(const Fp16AttnArgs& a, const float* ex, int b, int g, int G) {
+    const int ns = a.n_splits;
+    for (int k = threadIdx.x; k < G * a.d0; k += blockDim.x) {
+        const int n = k / a.d0, j = k % a.d0;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, ex[((size_t)s * G + n) * (D + 2)]);
+        float L = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const float ms = ex[((size_t)s * G + n) * (D + 2)];
+            if (ms != -INFINITY) L += ex[((size_t)s * G + n) * (D + 2) + 1] * exp2f((ms - M) * kLog2eF);
+        }
+        float v = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const float ms = ex[((size_t)s * G + n) * (D + 2)];
+            if (ms != -INFINITY) v += ex[((size_t)s * G + n) * (D + 2) + 2 + j] * exp2f((ms - M) * kLog2eF);
+        }
+        a.out[((size_t)b * a.n_q_heads + g * G + n) * a.d0 + j] = (L > 0.0f) ? v / L : 0.0f;
+    }
+}
+
+template <int D, bool MERGE>
 __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) {
     using S = Fp16Step<D>;
     constexpr int TS = S::TS, NMB = S::NMB, NCH = S::NCH, NKB = S::NKB, VCPL = S::VCPL;
@@ -90,12 +118,19 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
     const int64_t s0 = 0;
     const int64_t s1 = split < nsteps ? (nsteps - split + a.n_splits - 1) / a.n_splits : 0;
     auto step_of = [&](int64_t k) { return (int64_t)split + (k < s1 ? k : s1 - 1) * a.n_splits; };
+    // the split's partial: in the workspace, or (MERGE) in LDS for the workgroup
+    extern __shared__ __align__(16) float ex[];
     auto part = [&](int n) {
+        if constexpr (MERGE) return ex + ((size_t)split * G + n) * (D + 2);
         return a.ws + (((size_t)b * a.n_q_heads + g * G + n) * a.n_splits + split) * (D + 2);
     };
     if (s0 >= s1) {
         for (int k = lane; k < G * (D + 2); k += 64)
             part(k / (D + 2))[k % (D + 2)] = (k % (D + 2) == 0) ? -INFINITY : 0.0f;
+        if constexpr (MERGE) {
+            __syncthreads();
+            fp16_merge_in_block<D>(a, ex, b, g, G);
+        }
         return;
     }
     const int mrow = lane & 15, mgrp = lane >> 4;
@@ -266,6 +301,10 @@ __global__ __launch_bounds__(256) void attn_fp16_partial_kernel(Fp16AttnArgs a) 
         p[0] = m_run;
         p[1] = l_run;
     }
+    if constexpr (MERGE) {
+        __syncthreads();
+        fp16_merge_in_block<D>(a, ex, b, g, G);
+    }
 }
 
 template <int D>
@@ -294,11 +333,20 @@ __global__ __launch_bounds__(256) void attn_fp16_combine_kernel(Fp16AttnArgs a) 
 // tiles, so one instantiation per head_dim serves every group size.
 template <int D>
 hipError_t launch_f16(const Fp16AttnArgs& a, hipStream_t s) {
+    if (a.n_splits > 0 && a.n_splits <= 4) {
+        // a (b, g)'s splits fit one workgroup: they run as its waves and merge
+        // there through n_splits x G x (D + 2) floats of LDS, no combine launch
+        const int G = a.n_q_heads / a.n_kv_heads;
+        const size_t lds = (size_t)a.n_splits * G * (D + 2) * sizeof(float);
+        hipLaunchKernelGGL((attn_fp16_partial_kernel<D, true>), dim3((unsigned)((int64_t)a.batch * a.n_kv_heads)),
+                           dim3(64 * a.n_splits), lds, s, a);
+        return hipGetLastError();
+    }
     if (a.n_splits > 0) {
         constexpr int wpb = 4;
         const int64_t sgroups = (a.n_splits + wpb - 1) / wpb;
         const int64_t blocks = (int64_t)a.batch * a.n_kv_heads * sgroups;
-        hipLaunchKernelGGL((attn_fp16_partial_kernel<D>), dim3((unsigned)blocks), dim3(64 * wpb),
+        hipLaunchKernelGGL((attn_fp16_partial_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * wpb),
                            0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
